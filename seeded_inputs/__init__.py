@@ -1,0 +1,11 @@
+"""Seeded synthetic inputs for S2-Attn, shared by the tests, the bench and the oracle.
+
+This package holds workload shapes and random draws only. It contains none of
+the attention arithmetic: the GPU path and the CPU oracle each implement the
+method on their own and meet only here, on identical input values.
+"""
+
+from .configs import CONFIGS, Workload, workload
+from .gen import bf16_round, bf16_bits, make_inputs
+
+__all__ = ["CONFIGS", "Workload", "workload", "bf16_round", "bf16_bits", "make_inputs"]
