@@ -1,0 +1,141 @@
+/*
+ * libs2attn -- S2-Attn (shift short attention, from LongLoRA) on MI355X (gfx950).
+ *
+ * The operation (LongLoRA blog summary, smallflyingpig.github.io, section 3.3;
+ * nearauto.com LongLoRA article, shift-short-attention section; python88.com
+ * LongLoRA article, section on reducing computation):
+ *   A sequence of L tokens is cut into L/G groups of G tokens and causal
+ *   softmax attention runs only inside each group.  The last `shifted_heads`
+ *   query heads see the sequence rolled left by G/2 (token t sits at rolled
+ *   position (t - G/2) mod L) before grouping, and their outputs are rolled
+ *   back, so groups of shifted and unshifted heads overlap.  Causality is by
+ *   in-group index in the rolled order; the roll is cyclic, so the last
+ *   shifted group holds the last G/2 tokens followed by the first G/2.
+ *   The roll, grouping and un-roll are address arithmetic in the kernels: no
+ *   copy of any tensor is made.
+ *
+ * Layout (all tensors contiguous, row-major):
+ *   q, o, dout, dq : [B, L, Hq, d]
+ *   k, v, dk, dv   : [B, L, Hkv, d]      query head h uses KV head h / (Hq/Hkv)
+ *   lse, delta     : [B, Hq, L] float32, indexed by original token position
+ *   lse[b,h,t] = ln sum_j exp(scale * q_t . k_j) over the keys t may attend to.
+ *
+ * Conventions for every entry point:
+ *   - Pointers are device memory owned by the caller; the library allocates
+ *     nothing and keeps nothing after it returns.  Pointers must be 16-byte
+ *     aligned.  Outputs must not alias inputs.  Outputs are overwritten, not
+ *     accumulated into (dk, dv already hold the sum over the query heads that
+ *     share a KV head).
+ *   - Calls only enqueue work on `stream` (0 = the default stream).  The
+ *     returned status covers argument checks and kernel launch; faults during
+ *     execution surface at the caller's next synchronisation.
+ *   - Every argument check runs on the host before any HIP call, so invalid
+ *     arguments are reported without touching the GPU.  Nothing is printed.
+ *   - Stateless and thread-safe.
+ */
+#ifndef S2ATTN_H
+#define S2ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    S2ATTN_OK = 0,
+    S2ATTN_ERR_INVALID_ARG = 1,  /* null pointer, size <= 0, L % G != 0, odd G with shifted
+                                    heads, Hq % Hkv != 0, shifted_heads outside [0, Hq],
+                                    bad opts (struct_size, dtype, rope fields) */
+    S2ATTN_ERR_UNSUPPORTED = 2,  /* d not in {64, 128}; shifted_heads % (Hq/Hkv) != 0 (a KV
+                                    head shared by shifted and unshifted query heads); bf16
+                                    path with G % 128 != 0 or (shifted) G/2 % 64 != 0;
+                                    RoPE with float32 inputs */
+    S2ATTN_ERR_WORKSPACE = 3,    /* workspace missing or smaller than s2attn_workspace_size() */
+    S2ATTN_ERR_HIP = 4           /* a HIP runtime error (no device, launch failure, ...) */
+} s2attn_status;
+
+typedef enum {
+    S2ATTN_BF16 = 0,
+    S2ATTN_F32 = 1
+} s2attn_dtype;
+
+/*
+ * Options for the _ex entry points.  Fill with s2attn_opts_init() first.
+ *   dtype        element type of q, k, v, o, dout.  BF16: bf16 MFMA with fp32
+ *                accumulation; F32: fp32 arithmetic throughout.
+ *   grad_dtype   element type of dq, dk, dv (BF16 only with bf16 inputs, or F32).
+ *   softmax_scale  <= 0 selects 1/sqrt(d).
+ *   rope         nonzero: rotate q and k at their original positions t by
+ *                angle t * (rope_orig_len / L) * rope_base^(-2c/d) on channel
+ *                pairs (c, c + d/2), c < d/2, before attention (RoPE with
+ *                position interpolation, LongLoRA blog section 3.4).
+ *                Gradients are then w.r.t. the un-rotated q and k.
+ */
+typedef struct {
+    uint32_t struct_size;  /* must equal sizeof(s2attn_opts) */
+    int32_t dtype;
+    int32_t grad_dtype;
+    float softmax_scale;
+    int32_t rope;
+    float rope_base;
+    int32_t rope_orig_len;
+} s2attn_opts;
+
+/* Defaults: bf16 inputs and gradients, scale 1/sqrt(d), no RoPE. */
+void s2attn_opts_init(s2attn_opts* opts);
+
+/*
+ * Forward, bf16, scale 1/sqrt(d), no RoPE.
+ * Reads q, k, v; writes o (bf16) and lse (fp32).
+ */
+int s2attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int L, int Hq, int Hkv, int d, int G, int shifted_heads,
+               hipStream_t stream);
+
+/*
+ * Backward, bf16 inputs and gradients, scale 1/sqrt(d), no RoPE.
+ * Reads q, k, v, o, lse (as written by s2attn_fwd on the same inputs) and
+ * dout; writes dq, dk, dv.  delta_ws is caller scratch of B*Hq*L floats
+ * (receives rowsum(dout * o)).  Gradient formulas: with P the attention
+ * probabilities, dS = P * (dout . v_j - delta), dq = scale dS k,
+ * dk = scale dS^T q, dv = P^T dout (summed over query heads per KV head).
+ */
+int s2attn_bwd(const void* q, const void* k, const void* v, const void* o,
+               const float* lse, const void* dout, void* dq, void* dk, void* dv,
+               float* delta_ws,
+               int B, int L, int Hq, int Hkv, int d, int G, int shifted_heads,
+               hipStream_t stream);
+
+/*
+ * Bytes of workspace the _ex entry points need for these sizes and options
+ * (0 when none).  is_bwd selects the backward.  Returns 0 for invalid
+ * arguments as well; the _ex call then reports the error.
+ */
+size_t s2attn_workspace_size(int is_bwd, int B, int L, int Hq, int Hkv, int d, int G,
+                             const s2attn_opts* opts);
+
+/* Forward with options; `ws` may be NULL when the workspace size is 0. */
+int s2attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int B, int L, int Hq, int Hkv, int d, int G, int shifted_heads,
+                  const s2attn_opts* opts, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Backward with options; the row term delta lives in the workspace. */
+int s2attn_bwd_ex(const void* q, const void* k, const void* v, const void* o,
+                  const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                  int B, int L, int Hq, int Hkv, int d, int G, int shifted_heads,
+                  const s2attn_opts* opts, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Static string naming a status code. */
+const char* s2attn_status_string(int status);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int s2attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* S2ATTN_H */

@@ -1,1 +1,82 @@
-"""libs2attn: S2-Attn (LongLoRA shift short attention) forward and backward for MI355X."""
+"""libs2attn: S2-Attn (LongLoRA's shift short attention) forward and backward on MI355X.
+
+The C entry points are re-exported under their own names (`s2attn_fwd`,
+`s2attn_bwd`, `s2attn_fwd_ex`, `s2attn_bwd_ex`, `s2attn_workspace_size`, ...).
+`forward` and `backward` allocate outputs with torch and call them.
+
+Tensors are [B, L, H, d] contiguous (q, o, dout: H = Hq; k, v: H = Hkv); LSE
+is [B, Hq, L] float32.  The last `shifted_heads` query heads attend within
+groups shifted by G/2 tokens.
+"""
+
+import math
+
+import torch
+
+from . import flops  # noqa: F401
+from ._lib import (  # noqa: F401
+    LIB_PATH, S2ATTN_BF16, S2ATTN_ERR_HIP, S2ATTN_ERR_INVALID_ARG, S2ATTN_ERR_UNSUPPORTED,
+    S2ATTN_ERR_WORKSPACE, S2ATTN_F32, S2ATTN_OK, S2AttnError, lib, s2attn_bwd, s2attn_bwd_ex,
+    s2attn_fwd, s2attn_fwd_ex, s2attn_opts, s2attn_opts_init, s2attn_status_string,
+    s2attn_version, s2attn_workspace_size)
+
+_DT = {torch.bfloat16: S2ATTN_BF16, torch.float32: S2ATTN_F32}
+
+
+def _shapes(q, k, v):
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("q must be [B, L, Hq, d]; k and v [B, L, Hkv, d]")
+    B, L, Hq, d = q.shape
+    if k.shape[0] != B or k.shape[1] != L or k.shape[3] != d:
+        raise ValueError("k, v must match q in B, L and d")
+    for t in (q, k, v):
+        if not t.is_contiguous() or t.dtype != q.dtype:
+            raise ValueError("q, k, v must be contiguous and of one dtype")
+    return B, L, Hq, k.shape[2], d
+
+
+def make_opts(dtype, grad_dtype=None, scale=None, rope=None):
+    """Build s2attn_opts.  `rope` is None or (base, orig_len)."""
+    o = s2attn_opts_init()
+    o.dtype = _DT[dtype]
+    o.grad_dtype = _DT[grad_dtype if grad_dtype is not None else dtype]
+    o.softmax_scale = 0.0 if scale is None else float(scale)
+    if rope is not None:
+        o.rope = 1
+        o.rope_base = float(rope[0])
+        o.rope_orig_len = int(rope[1])
+    return o
+
+
+def forward(q, k, v, G, shifted_heads, *, scale=None, rope=None, stream=None):
+    """S2-Attn forward.  Returns (o, lse)."""
+    B, L, Hq, Hkv, d = _shapes(q, k, v)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, L), dtype=torch.float32, device=q.device)
+    opts = make_opts(q.dtype, scale=scale, rope=rope)
+    ws_bytes = s2attn_workspace_size(0, B, L, Hq, Hkv, d, G, opts)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device) if ws_bytes else None
+    s2attn_fwd_ex(q, k, v, o, lse, B, L, Hq, Hkv, d, G, shifted_heads, opts, ws, ws_bytes, stream)
+    return o, lse
+
+
+def backward(q, k, v, o, lse, dout, G, shifted_heads, *, scale=None, rope=None,
+             grad_dtype=None, stream=None):
+    """S2-Attn backward.  Returns (dq, dk, dv) in `grad_dtype` (default: q's dtype)."""
+    B, L, Hq, Hkv, d = _shapes(q, k, v)
+    if dout.shape != q.shape or o.shape != q.shape or lse.shape != (B, Hq, L):
+        raise ValueError("o and dout must match q; lse must be [B, Hq, L]")
+    gd = grad_dtype if grad_dtype is not None else q.dtype
+    dq = torch.empty(q.shape, dtype=gd, device=q.device)
+    dk = torch.empty(k.shape, dtype=gd, device=q.device)
+    dv = torch.empty(v.shape, dtype=gd, device=q.device)
+    opts = make_opts(q.dtype, grad_dtype=gd, scale=scale, rope=rope)
+    ws_bytes = s2attn_workspace_size(1, B, L, Hq, Hkv, d, G, opts)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    s2attn_bwd_ex(q, k, v, o, lse, dout, dq, dk, dv, B, L, Hq, Hkv, d, G, shifted_heads,
+                  opts, ws, ws_bytes, stream)
+    return dq, dk, dv
+
+
+def default_scale(d):
+    return 1.0 / math.sqrt(d)

@@ -1,0 +1,128 @@
+// Device helpers shared by the S2-Attn kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "s2_params.h"
+
+namespace s2 {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------------------
+// Index map.  Head h with shift s reads the sequence rolled left by s: the
+// token at rolled position p is original token (p + s) mod L.  In-group index
+// i of group g is rolled position g*G + i.  (LongLoRA blog, section 3.3,
+// worked shift example: shifted groups start half a group later, wrapping.)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int orig_row(int g, int G, int i, int s, int L) {
+    int t = g * G + i + s;
+    return t >= L ? t - L : t;
+}
+
+// ---------------------------------------------------------------------------
+// Row-major bf16 tiles of 128 (or 64) columns in LDS, 16-byte slots swizzled
+// by an XOR of the row so that both access patterns the kernels use spread
+// over the banks: 32 rows read at one 16-byte column slot (MFMA operand from
+// a row-major tile) and 4 rows x 32 bytes per 16 lanes (transposed reads).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int swz(int row) {
+    return ((row & 3) << 1) | ((row >> 2) & 1);
+}
+
+// Byte offset of element (row, col) in a row-major tile with `D` bf16 columns.
+template <int D>
+__device__ __forceinline__ int tile_off(int row, int col) {
+    int slot = (col >> 3) ^ swz(row);
+    return row * (D * 2) + slot * 16 + (col & 7) * 2;
+}
+
+// 16-byte global load / LDS store / LDS load.
+__device__ __forceinline__ u32x4 ld_global16(const void* p) {
+    return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ void st_lds16(char* lds, int off, u32x4 v) {
+    *reinterpret_cast<u32x4*>(lds + off) = v;
+}
+__device__ __forceinline__ bf16x8 ld_lds16(const char* lds, int off) {
+    return *reinterpret_cast<const bf16x8*>(lds + off);
+}
+
+// Transposed LDS read (gfx950 ds_read_b64_tr_b16).  Within each 16-lane
+// group, lane j supplies the address of 4 consecutive bf16 (8 bytes);
+// result lane i receives, in slot s, element (i % 4) of source lane 4s + i/4.
+// With source lane j pointing at row r0 + j/4, columns c0 + 4(j%4) .. +3,
+// result lane i gets column c0 + i of rows r0 .. r0+3.
+__device__ __forceinline__ bf16x4 ld_lds_tr(const char* lds, int off) {
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(const_cast<char*>(lds) + off));
+    return __builtin_bit_cast(bf16x4, r);
+}
+
+__device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// 32x32x16 bf16 MFMA.  Lane l holds A[l%32][8(l/32) + 0..7] and
+// B[8(l/32) + 0..7][l%32]; C[8j + 4(l/32) + k][l%32] is acc[4j + k].
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// max / sum with the lane 32 apart (v_permlane32_swap gives both halves' values).
+__device__ __forceinline__ float xhalf_max(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ bf16x8 to_bf16x8(const float* x) {
+    bf16x8 r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = (bf16)x[i];
+    return r;
+}
+
+// Work decode shared by the tiled kernels: unit (b, h, g) and tile index
+// from the flat block id.  Workgroups are dispatched round-robin over the 8
+// XCDs; when the unit count is a multiple of 8, every tile of a unit lands
+// on the same XCD (so its K/V stay in that XCD's L2), and tiles of a unit
+// are issued longest-first.
+struct Work {
+    int b, h, g, tile;
+};
+
+__device__ __forceinline__ Work decode_work(int bid, int n_units, int n_tiles, int Hh, int n_g) {
+    int u, t;
+    if ((n_units & 7) == 0) {
+        int xcd = bid & 7, slot = bid >> 3;
+        u = (slot / n_tiles) * 8 + xcd;
+        t = slot % n_tiles;
+    } else {
+        u = bid / n_tiles;
+        t = bid % n_tiles;
+    }
+    Work w;
+    w.g = u % n_g;
+    int bh = u / n_g;
+    w.h = bh % Hh;
+    w.b = bh / Hh;
+    w.tile = n_tiles - 1 - t;  // longest first
+    return w;
+}
+
+}  // namespace s2

@@ -1,0 +1,58 @@
+// Launch parameters passed by value to every S2-Attn kernel.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace s2 {
+
+struct Params {
+    // Tensors.  Element types follow the dtype fields of the launcher.
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;
+    const void* dout;
+    void* dq;
+    void* dk;
+    void* dv;
+    float* delta;
+    // Sizes.
+    int B, L, Hq, Hkv, d, G, shifted_heads;
+    int r;          // Hq / Hkv
+    int n_g;        // L / G
+    float scale;    // softmax scale
+    float scale_log2;  // scale * log2(e)
+    // RoPE with position interpolation: angle = t * rope_pos_scale * rope_base^(-2c/d).
+    int rope;
+    float rope_base;
+    double rope_pos_scale;
+};
+
+// Head shift: half a group for the last `shifted_heads` query heads.
+__host__ __device__ inline int head_shift(const Params& p, int h) {
+    return h >= p.Hq - p.shifted_heads ? p.G / 2 : 0;
+}
+
+// Row strides (in elements) of the [B, L, H, d] layouts.
+__host__ __device__ inline size_t q_row(const Params& p, int b, int t, int h) {
+    return ((size_t)(b * (size_t)p.L + t) * p.Hq + h) * p.d;
+}
+__host__ __device__ inline size_t kv_row(const Params& p, int b, int t, int h) {
+    return ((size_t)(b * (size_t)p.L + t) * p.Hkv + h) * p.d;
+}
+__host__ __device__ inline size_t lse_idx(const Params& p, int b, int h, int t) {
+    return ((size_t)b * p.Hq + h) * p.L + t;
+}
+
+// Launchers (one per kernel family).  Return hipSuccess or the launch error.
+hipError_t launch_fwd_bf16(const Params& p, hipStream_t s);
+hipError_t launch_fwd_f32(const Params& p, hipStream_t s);
+hipError_t launch_bwd_pre(const Params& p, int f32_io, hipStream_t s);
+hipError_t launch_bwd_bf16(const Params& p, int grad_f32, hipStream_t s);
+hipError_t launch_bwd_f32(const Params& p, hipStream_t s);
+hipError_t launch_rope_prepass(const Params& p, void* q_out, void* k_out, hipStream_t s);
+
+}  // namespace s2

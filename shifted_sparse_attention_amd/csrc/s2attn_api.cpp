@@ -1,0 +1,276 @@
+// libs2attn C ABI: argument checks, workspace sizing and kernel dispatch.
+//
+// Every check below is pure host arithmetic and runs before the first HIP
+// call, so invalid arguments are reported without touching a device.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "s2_params.h"
+#include "s2attn.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Resolved {
+    int dtype;       // S2ATTN_BF16 / S2ATTN_F32
+    int grad_dtype;
+    float scale;
+    int rope;
+    float rope_base;
+    int rope_orig_len;
+};
+
+// Sizes shared by forward and backward.
+int check_sizes(int B, int L, int Hq, int Hkv, int d, int G, int shifted_heads) {
+    if (B <= 0 || L <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || G <= 0) return S2ATTN_ERR_INVALID_ARG;
+    if (L % G != 0) return S2ATTN_ERR_INVALID_ARG;
+    if (Hq % Hkv != 0) return S2ATTN_ERR_INVALID_ARG;
+    if (shifted_heads < 0 || shifted_heads > Hq) return S2ATTN_ERR_INVALID_ARG;
+    if (shifted_heads > 0 && (G % 2) != 0) return S2ATTN_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return S2ATTN_ERR_UNSUPPORTED;
+    // Element counts must fit the 64-bit offsets; workgroup counts fit a 32-bit grid.
+    const double elems = (double)B * L * Hq * d;
+    if (elems > 9.0e18) return S2ATTN_ERR_UNSUPPORTED;
+    const double wgs = (double)B * Hq * (L / G) * ((G + 63) / 64);
+    if (wgs > 2147483647.0) return S2ATTN_ERR_UNSUPPORTED;
+    if ((double)L * Hq > 2147483647.0) return S2ATTN_ERR_UNSUPPORTED;
+    return S2ATTN_OK;
+}
+
+int resolve_opts(const s2attn_opts* o, int d, Resolved* r) {
+    s2attn_opts def;
+    s2attn_opts_init(&def);
+    if (o == nullptr) o = &def;
+    if (o->struct_size != sizeof(s2attn_opts)) return S2ATTN_ERR_INVALID_ARG;
+    if (o->dtype != S2ATTN_BF16 && o->dtype != S2ATTN_F32) return S2ATTN_ERR_INVALID_ARG;
+    if (o->grad_dtype != S2ATTN_BF16 && o->grad_dtype != S2ATTN_F32) return S2ATTN_ERR_INVALID_ARG;
+    if (isnan(o->softmax_scale) || isinf(o->softmax_scale)) return S2ATTN_ERR_INVALID_ARG;
+    if (o->rope) {
+        if (!(o->rope_base > 1.0f) || isinf(o->rope_base)) return S2ATTN_ERR_INVALID_ARG;
+        if (o->rope_orig_len <= 0) return S2ATTN_ERR_INVALID_ARG;
+        if (o->dtype == S2ATTN_F32) return S2ATTN_ERR_UNSUPPORTED;
+    }
+    if (o->dtype == S2ATTN_F32 && o->grad_dtype == S2ATTN_BF16) return S2ATTN_ERR_UNSUPPORTED;
+    r->dtype = o->dtype;
+    r->grad_dtype = o->grad_dtype;
+    r->scale = o->softmax_scale > 0.f ? o->softmax_scale : 1.0f / sqrtf((float)d);
+    r->rope = o->rope ? 1 : 0;
+    r->rope_base = o->rope_base;
+    r->rope_orig_len = o->rope_orig_len;
+    return S2ATTN_OK;
+}
+
+size_t elem_size(int dtype) { return dtype == S2ATTN_F32 ? 4 : 2; }
+
+// Workspace layout: [delta (bwd) | rotated q | rotated k], each 256-byte aligned.
+struct WsLayout {
+    size_t delta_off, delta_bytes;
+    size_t rq_off, rq_bytes;
+    size_t rk_off, rk_bytes;
+    size_t total;
+};
+
+WsLayout ws_layout(int is_bwd, int B, int L, int Hq, int Hkv, int d, const Resolved& r) {
+    WsLayout w{};
+    size_t off = 0;
+    if (is_bwd) {
+        w.delta_off = off;
+        w.delta_bytes = (size_t)B * Hq * L * sizeof(float);
+        off += align_up(w.delta_bytes);
+    }
+    if (r.rope) {
+        w.rq_off = off;
+        w.rq_bytes = (size_t)B * L * Hq * d * 2;
+        off += align_up(w.rq_bytes);
+        w.rk_off = off;
+        w.rk_bytes = (size_t)B * L * Hkv * d * 2;
+        off += align_up(w.rk_bytes);
+    }
+    w.total = off;
+    return w;
+}
+
+s2::Params make_params(int B, int L, int Hq, int Hkv, int d, int G, int shifted_heads,
+                       const Resolved& r) {
+    s2::Params p;
+    memset(&p, 0, sizeof(p));
+    p.B = B;
+    p.L = L;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.d = d;
+    p.G = G;
+    p.shifted_heads = shifted_heads;
+    p.r = Hq / Hkv;
+    p.n_g = L / G;
+    p.scale = r.scale;
+    p.scale_log2 = r.scale * 1.4426950408889634f;
+    p.rope = r.rope;
+    p.rope_base = r.rope_base;
+    p.rope_pos_scale = (double)r.rope_orig_len / (double)L;
+    return p;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? S2ATTN_OK : S2ATTN_ERR_HIP; }
+
+int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int L,
+             int Hq, int Hkv, int d, int G, int shifted_heads, const s2attn_opts* opts, void* ws,
+             size_t ws_bytes, hipStream_t stream) {
+    if (!q || !k || !v || !o || !lse) return S2ATTN_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+        return S2ATTN_ERR_INVALID_ARG;
+    int st = check_sizes(B, L, Hq, Hkv, d, G, shifted_heads);
+    if (st) return st;
+    Resolved r;
+    st = resolve_opts(opts, d, &r);
+    if (st) return st;
+    const WsLayout wl = ws_layout(0, B, L, Hq, Hkv, d, r);
+    if (wl.total > 0 && (ws == nullptr || ws_bytes < wl.total || !aligned16(ws)))
+        return S2ATTN_ERR_WORKSPACE;
+
+    s2::Params p = make_params(B, L, Hq, Hkv, d, G, shifted_heads, r);
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.o = o;
+    p.lse = lse;
+    if (r.dtype == S2ATTN_F32) return hip_status(s2::launch_fwd_f32(p, stream));
+    if (r.rope) {
+        char* base = static_cast<char*>(ws);
+        void* rq = base + wl.rq_off;
+        void* rk = base + wl.rk_off;
+        hipError_t e = s2::launch_rope_prepass(p, rq, rk, stream);
+        if (e != hipSuccess) return S2ATTN_ERR_HIP;
+        p.q = rq;
+        p.k = rk;
+        p.rope = 0;  // the forward's outputs need no rotation back
+    }
+    return hip_status(s2::launch_fwd_bf16(p, stream));
+}
+
+int bwd_impl(const void* q, const void* k, const void* v, const void* o, const float* lse,
+             const void* dout, void* dq, void* dk, void* dv, float* delta, int B, int L, int Hq,
+             int Hkv, int d, int G, int shifted_heads, const s2attn_opts* opts, void* ws,
+             size_t ws_bytes, hipStream_t stream) {
+    if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return S2ATTN_ERR_INVALID_ARG;
+    const void* ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv};
+    for (const void* ptr : ptrs)
+        if (!aligned16(ptr)) return S2ATTN_ERR_INVALID_ARG;
+    int st = check_sizes(B, L, Hq, Hkv, d, G, shifted_heads);
+    if (st) return st;
+    Resolved r;
+    st = resolve_opts(opts, d, &r);
+    if (st) return st;
+    if (shifted_heads % (Hq / Hkv) != 0) return S2ATTN_ERR_UNSUPPORTED;
+
+    WsLayout wl = ws_layout(1, B, L, Hq, Hkv, d, r);
+    char* base = static_cast<char*>(ws);
+    if (delta != nullptr) {
+        // Plain entry point: delta supplied separately, workspace holds the rest.
+        if (!aligned16(delta)) return S2ATTN_ERR_INVALID_ARG;
+        wl = ws_layout(0, B, L, Hq, Hkv, d, r);
+    }
+    if (wl.total > 0 && (ws == nullptr || ws_bytes < wl.total || !aligned16(ws)))
+        return S2ATTN_ERR_WORKSPACE;
+    if (delta == nullptr) delta = reinterpret_cast<float*>(base + wl.delta_off);
+
+    s2::Params p = make_params(B, L, Hq, Hkv, d, G, shifted_heads, r);
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.o = const_cast<void*>(o);
+    p.lse = const_cast<float*>(lse);
+    p.dout = dout;
+    p.dq = dq;
+    p.dk = dk;
+    p.dv = dv;
+    p.delta = delta;
+
+    hipError_t e = s2::launch_bwd_pre(p, r.dtype == S2ATTN_F32, stream);
+    if (e != hipSuccess) return S2ATTN_ERR_HIP;
+    if (r.dtype == S2ATTN_F32) return hip_status(s2::launch_bwd_f32(p, stream));
+    if (r.rope) {
+        void* rq = base + wl.rq_off;
+        void* rk = base + wl.rk_off;
+        e = s2::launch_rope_prepass(p, rq, rk, stream);
+        if (e != hipSuccess) return S2ATTN_ERR_HIP;
+        p.q = rq;
+        p.k = rk;  // p.rope stays set: the epilogues rotate dq, dk back
+    }
+    return hip_status(s2::launch_bwd_bf16(p, r.grad_dtype == S2ATTN_F32, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+void s2attn_opts_init(s2attn_opts* opts) {
+    if (!opts) return;
+    memset(opts, 0, sizeof(*opts));
+    opts->struct_size = sizeof(s2attn_opts);
+    opts->dtype = S2ATTN_BF16;
+    opts->grad_dtype = S2ATTN_BF16;
+    opts->softmax_scale = 0.f;
+    opts->rope = 0;
+    opts->rope_base = 10000.f;
+    opts->rope_orig_len = 4096;
+}
+
+int s2attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int L,
+               int Hq, int Hkv, int d, int G, int shifted_heads, hipStream_t stream) {
+    return fwd_impl(q, k, v, o, lse, B, L, Hq, Hkv, d, G, shifted_heads, nullptr, nullptr, 0,
+                    stream);
+}
+
+int s2attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+               const void* dout, void* dq, void* dk, void* dv, float* delta_ws, int B, int L,
+               int Hq, int Hkv, int d, int G, int shifted_heads, hipStream_t stream) {
+    if (!delta_ws) return S2ATTN_ERR_INVALID_ARG;
+    return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, delta_ws, B, L, Hq, Hkv, d, G,
+                    shifted_heads, nullptr, nullptr, 0, stream);
+}
+
+size_t s2attn_workspace_size(int is_bwd, int B, int L, int Hq, int Hkv, int d, int G,
+                             const s2attn_opts* opts) {
+    if (check_sizes(B, L, Hq, Hkv, d, G, 0) != S2ATTN_OK) return 0;
+    Resolved r;
+    if (resolve_opts(opts, d, &r) != S2ATTN_OK) return 0;
+    return ws_layout(is_bwd ? 1 : 0, B, L, Hq, Hkv, d, r).total;
+}
+
+int s2attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int L,
+                  int Hq, int Hkv, int d, int G, int shifted_heads, const s2attn_opts* opts,
+                  void* ws, size_t ws_bytes, hipStream_t stream) {
+    return fwd_impl(q, k, v, o, lse, B, L, Hq, Hkv, d, G, shifted_heads, opts, ws, ws_bytes,
+                    stream);
+}
+
+int s2attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                  const void* dout, void* dq, void* dk, void* dv, int B, int L, int Hq, int Hkv,
+                  int d, int G, int shifted_heads, const s2attn_opts* opts, void* ws,
+                  size_t ws_bytes, hipStream_t stream) {
+    return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, nullptr, B, L, Hq, Hkv, d, G,
+                    shifted_heads, opts, ws, ws_bytes, stream);
+}
+
+const char* s2attn_status_string(int status) {
+    switch (status) {
+        case S2ATTN_OK: return "S2ATTN_OK";
+        case S2ATTN_ERR_INVALID_ARG: return "S2ATTN_ERR_INVALID_ARG";
+        case S2ATTN_ERR_UNSUPPORTED: return "S2ATTN_ERR_UNSUPPORTED";
+        case S2ATTN_ERR_WORKSPACE: return "S2ATTN_ERR_WORKSPACE";
+        case S2ATTN_ERR_HIP: return "S2ATTN_ERR_HIP";
+        default: return "S2ATTN_UNKNOWN_STATUS";
+    }
+}
+
+int s2attn_version(void) { return 100; }
+
+}  // extern "C"

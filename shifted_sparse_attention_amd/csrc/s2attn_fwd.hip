@@ -1,0 +1,271 @@
+// S2-Attn forward kernels.
+//
+// One workgroup computes a tile of queries of one group of one head (a unit
+// (b, h, g)).  Rows are read and written at their original positions through
+// the roll map (orig_row), so the roll / regroup / un-roll of the method
+// (nearauto.com LongLoRA article, shift-short-attention section: shift half
+// the heads, then fold groups into the batch) never materialises a copy.
+// Causal masking uses in-group indices in rolled order.
+#include <math.h>
+
+#include "s2_device.h"
+
+namespace s2 {
+
+// ---------------------------------------------------------------------------
+// bf16 forward.  4 waves x 32 queries; K and V tiles of 64 keys staged in LDS.
+// Scores are formed transposed, S^T = K Q^T, so a lane owns one query column
+// and 16 of the 32 keys of each 32-key block (the other 16 sit in lane ^ 32):
+// the row max needs one permlane32 swap, the row sum none until the end.
+// P^T feeds O^T += V^T P^T directly from the score registers; V is read from
+// its row-major tile with transposed LDS reads.
+// ---------------------------------------------------------------------------
+constexpr int FWD_BM = 128;
+constexpr int FWD_BN = 64;
+constexpr int FWD_THREADS = 256;
+
+template <int D>
+__global__ __launch_bounds__(FWD_THREADS) void fwd_bf16_kernel(Params p, int n_qt) {
+    constexpr int KS = D / 16;  // MFMA k-steps over the head dimension
+    constexpr int CB = D / 32;  // 32-channel blocks of the output
+    __shared__ __attribute__((aligned(16))) char smem[2 * FWD_BN * D * 2];
+    char* sK = smem;
+    char* sV = smem + FWD_BN * D * 2;
+
+    const int n_units = p.B * p.Hq * p.n_g;
+    const Work w = decode_work(blockIdx.x, n_units, n_qt, p.Hq, p.n_g);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int hh = lane >> 5, l32 = lane & 31;
+    const int s = head_shift(p, w.h);
+    const int hk = w.h / p.r;
+    const bf16* __restrict__ q = static_cast<const bf16*>(p.q);
+    const bf16* __restrict__ k = static_cast<const bf16*>(p.k);
+    const bf16* __restrict__ v = static_cast<const bf16*>(p.v);
+
+    const int q0 = w.tile * FWD_BM;
+    const int qw = q0 + wave * 32;   // first query (in-group index) of this wave
+    const int qi = qw + l32;         // this lane's query
+    const bool q_valid = qi < p.G;
+    const int q_t = orig_row(w.g, p.G, q_valid ? qi : 0, s, p.L);
+
+    bf16x8 qf[KS];
+    {
+        const bf16* qr = q + q_row(p, w.b, q_t, w.h) + 8 * hh;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            u32x4 raw = q_valid ? ld_global16(qr + 16 * ks) : u32x4{0, 0, 0, 0};
+            qf[ks] = __builtin_bit_cast(bf16x8, raw);
+        }
+    }
+
+    f32x16 oacc[CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) oacc[cb] = f32x16{};
+    float m = -INFINITY, lsum = 0.f;
+
+    const int q_end = min(q0 + FWD_BM, p.G);
+    const int n_kt = (q_end + FWD_BN - 1) / FWD_BN;
+    const int g16 = lane >> 4, jj = lane & 15;
+
+    for (int kt = 0; kt < n_kt; ++kt) {
+        const int k0 = kt * FWD_BN;
+        __syncthreads();
+        {
+            constexpr int CPR = D / 8;  // 16-byte chunks per row
+#pragma unroll
+            for (int c = tid; c < FWD_BN * CPR; c += FWD_THREADS) {
+                const int row = c / CPR, col = (c % CPR) * 8;
+                const int j = k0 + row;
+                u32x4 kr = {0, 0, 0, 0}, vr = {0, 0, 0, 0};
+                if (j < p.G) {
+                    const size_t off = kv_row(p, w.b, orig_row(w.g, p.G, j, s, p.L), hk) + col;
+                    kr = ld_global16(k + off);
+                    vr = ld_global16(v + off);
+                }
+                st_lds16(sK, tile_off<D>(row, col), kr);
+                st_lds16(sV, tile_off<D>(row, col), vr);
+            }
+        }
+        __syncthreads();
+        if (k0 > qw + 31) continue;  // every key of the tile is after every query of the wave
+
+        f32x16 sacc[2];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+            sacc[mb] = f32x16{};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                bf16x8 a = ld_lds16(sK, tile_off<D>(32 * mb + l32, 16 * ks + 8 * hh));
+                sacc[mb] = mfma32(a, qf[ks], sacc[mb]);
+            }
+        }
+
+        const bool diag = (k0 + FWD_BN - 1 > qw);
+        float mx = -INFINITY;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int key = k0 + 32 * mb + 8 * (i >> 2) + 4 * hh + (i & 3);
+                float x = sacc[mb][i] * p.scale_log2;
+                if (diag && key > qi) x = -INFINITY;
+                sacc[mb][i] = x;
+                mx = fmaxf(mx, x);
+            }
+        }
+        mx = xhalf_max(mx);
+        const float m_new = fmaxf(m, mx);
+        const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+        m = m_new;
+        float ps = 0.f;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float e = __builtin_amdgcn_exp2f(sacc[mb][i] - m_new);
+                sacc[mb][i] = e;
+                ps += e;
+            }
+        }
+        lsum = lsum * alpha + ps;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) oacc[cb] *= alpha;
+
+        bf16x8 pb[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            float tmp[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) tmp[i] = sacc[kk >> 1][8 * (kk & 1) + i];
+            pb[kk] = to_bf16x8(tmp);
+        }
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+            const int col = 32 * cb + 16 * (g16 & 1) + 4 * (jj & 3);
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const int row = 16 * kk + 4 * hh + (jj >> 2);
+                bf16x4 a0 = ld_lds_tr(sV, tile_off<D>(row, col));
+                bf16x4 a1 = ld_lds_tr(sV, tile_off<D>(row + 8, col));
+                oacc[cb] = mfma32(cat(a0, a1), pb[kk], oacc[cb]);
+            }
+        }
+    }
+
+    const float l_tot = xhalf_sum(lsum);
+    if (q_valid) {
+        const float inv = 1.0f / l_tot;
+        bf16* orow = static_cast<bf16*>(p.o) + q_row(p, w.b, q_t, w.h);
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                bf16x4 val;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) val[e] = (bf16)(oacc[cb][4 * j + e] * inv);
+                *reinterpret_cast<bf16x4*>(orow + 32 * cb + 8 * j + 4 * hh) = val;
+            }
+        }
+        if (hh == 0) p.lse[lse_idx(p, w.b, w.h, q_t)] = (m + log2f(l_tot)) * kLn2;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 forward: one thread per query row, 64 rows per workgroup, K/V tiles of
+// 64 keys in LDS, exact online softmax in natural exponentials.  Plain fp32
+// FMA arithmetic throughout.
+// ---------------------------------------------------------------------------
+constexpr int F32_ROWS = 64;
+
+template <int D>
+__global__ __launch_bounds__(F32_ROWS) void fwd_f32_kernel(Params p, int n_qt) {
+    __shared__ float sK[F32_ROWS][D];
+    __shared__ float sV[F32_ROWS][D];
+    const int n_units = p.B * p.Hq * p.n_g;
+    const Work w = decode_work(blockIdx.x, n_units, n_qt, p.Hq, p.n_g);
+    const int tid = threadIdx.x;
+    const int s = head_shift(p, w.h);
+    const int hk = w.h / p.r;
+    const float* __restrict__ q = static_cast<const float*>(p.q);
+    const float* __restrict__ k = static_cast<const float*>(p.k);
+    const float* __restrict__ v = static_cast<const float*>(p.v);
+
+    const int q0 = w.tile * F32_ROWS;
+    const int qi = q0 + tid;
+    const bool q_valid = qi < p.G;
+    const int q_t = orig_row(w.g, p.G, q_valid ? qi : 0, s, p.L);
+    float qr[D], acc[D];
+    const float* qp = q + q_row(p, w.b, q_t, w.h);
+#pragma unroll
+    for (int c = 0; c < D; ++c) {
+        qr[c] = q_valid ? qp[c] : 0.f;
+        acc[c] = 0.f;
+    }
+    float m = -INFINITY, l = 0.f;
+    const int q_end = min(q0 + F32_ROWS, p.G);
+    for (int k0 = 0; k0 < q_end; k0 += F32_ROWS) {
+        __syncthreads();
+        for (int e = tid; e < F32_ROWS * D; e += F32_ROWS) {
+            const int row = e / D, col = e % D, j = k0 + row;
+            float kv = 0.f, vv = 0.f;
+            if (j < p.G) {
+                const size_t off = kv_row(p, w.b, orig_row(w.g, p.G, j, s, p.L), hk) + col;
+                kv = k[off];
+                vv = v[off];
+            }
+            sK[row][col] = kv;
+            sV[row][col] = vv;
+        }
+        __syncthreads();
+        const int jmax = min(F32_ROWS, qi - k0 + 1);  // keys k0 .. qi
+        for (int j = 0; j < jmax; ++j) {
+            float dot = 0.f;
+#pragma unroll
+            for (int c = 0; c < D; ++c) dot = fmaf(qr[c], sK[j][c], dot);
+            const float x = dot * p.scale;
+            if (x > m) {
+                const float a = expf(m - x);
+                l *= a;
+#pragma unroll
+                for (int c = 0; c < D; ++c) acc[c] *= a;
+                m = x;
+            }
+            const float e = expf(x - m);
+            l += e;
+#pragma unroll
+            for (int c = 0; c < D; ++c) acc[c] = fmaf(e, sV[j][c], acc[c]);
+        }
+    }
+    if (q_valid) {
+        float* op = static_cast<float*>(p.o) + q_row(p, w.b, q_t, w.h);
+        const float inv = 1.0f / l;
+#pragma unroll
+        for (int c = 0; c < D; ++c) op[c] = acc[c] * inv;
+        p.lse[lse_idx(p, w.b, w.h, q_t)] = m + logf(l);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers.
+// ---------------------------------------------------------------------------
+hipError_t launch_fwd_bf16(const Params& p, hipStream_t st) {
+    const int n_qt = (p.G + FWD_BM - 1) / FWD_BM;
+    const long blocks = (long)p.B * p.Hq * p.n_g * n_qt;
+    if (p.d == 128)
+        hipLaunchKernelGGL(fwd_bf16_kernel<128>, dim3(blocks), dim3(FWD_THREADS), 0, st, p, n_qt);
+    else
+        hipLaunchKernelGGL(fwd_bf16_kernel<64>, dim3(blocks), dim3(FWD_THREADS), 0, st, p, n_qt);
+    return hipGetLastError();
+}
+
+hipError_t launch_fwd_f32(const Params& p, hipStream_t st) {
+    const int n_qt = (p.G + F32_ROWS - 1) / F32_ROWS;
+    const long blocks = (long)p.B * p.Hq * p.n_g * n_qt;
+    if (p.d == 128)
+        hipLaunchKernelGGL(fwd_f32_kernel<128>, dim3(blocks), dim3(F32_ROWS), 0, st, p, n_qt);
+    else
+        hipLaunchKernelGGL(fwd_f32_kernel<64>, dim3(blocks), dim3(F32_ROWS), 0, st, p, n_qt);
+    return hipGetLastError();
+}
+
+}  // namespace s2

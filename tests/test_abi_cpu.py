@@ -1,0 +1,177 @@
+"""libs2attn's C ABI on the host: loads, exports what the header declares, and
+rejects invalid arguments before any HIP call (so these run without a GPU).
+
+No valid compute call is made here: the addresses passed are fake (aligned,
+never dereferenced), and every case below fails an argument check first.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import shifted_sparse_attention_amd as s2
+from shifted_sparse_attention_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "s2attn.h")
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced
+MIS = 0x10008   # misaligned
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(s2attn_\w+)\s*\(", src)))
+
+
+def test_library_loads_and_exports_header_symbols():
+    h = L.lib()
+    names = declared_functions()
+    assert {"s2attn_fwd", "s2attn_bwd", "s2attn_fwd_ex", "s2attn_bwd_ex",
+            "s2attn_workspace_size", "s2attn_status_string"} <= set(names)
+    for n in names:
+        assert hasattr(h, n), n
+        assert n in L._SIGS, f"binding lacks {n}"
+        assert hasattr(s2, n), f"package does not re-export {n}"
+
+
+def test_single_hip_runtime_mapped():
+    L.lib()
+    assert len(L._hip_runtimes_mapped()) == 1
+
+
+def test_status_strings_and_version():
+    assert s2.s2attn_status_string(0) == "S2ATTN_OK"
+    assert s2.s2attn_status_string(1) == "S2ATTN_ERR_INVALID_ARG"
+    assert s2.s2attn_status_string(2) == "S2ATTN_ERR_UNSUPPORTED"
+    assert s2.s2attn_status_string(3) == "S2ATTN_ERR_WORKSPACE"
+    assert s2.s2attn_status_string(4) == "S2ATTN_ERR_HIP"
+    assert s2.s2attn_status_string(99) == "S2ATTN_UNKNOWN_STATUS"
+    assert s2.s2attn_version() >= 100
+
+
+def test_opts_defaults():
+    o = s2.s2attn_opts_init()
+    assert o.struct_size == ctypes.sizeof(L.s2attn_opts)
+    assert o.dtype == L.S2ATTN_BF16 and o.grad_dtype == L.S2ATTN_BF16
+    assert o.softmax_scale == 0.0 and o.rope == 0
+    assert o.rope_base == 10000.0 and o.rope_orig_len == 4096
+
+
+GOOD = dict(B=1, L=256, Hq=4, Hkv=4, d=64, G=64, sh=2)
+
+
+def fwd(**kw):
+    a = dict(GOOD, **kw)
+    ptrs = [kw.get(n, FAKE) for n in ("q", "k", "v", "o", "lse")]
+    return L.lib().s2attn_fwd(*ptrs, a["B"], a["L"], a["Hq"], a["Hkv"], a["d"], a["G"], a["sh"], None)
+
+
+def bwd(**kw):
+    a = dict(GOOD, **kw)
+    ptrs = [kw.get(n, FAKE) for n in ("q", "k", "v", "o", "lse", "do", "dq", "dk", "dv", "delta")]
+    return L.lib().s2attn_bwd(*ptrs, a["B"], a["L"], a["Hq"], a["Hkv"], a["d"], a["G"], a["sh"], None)
+
+
+def fwd_ex(opts, ws=None, ws_bytes=0, **kw):
+    a = dict(GOOD, **kw)
+    return L.lib().s2attn_fwd_ex(FAKE, FAKE, FAKE, FAKE, FAKE, a["B"], a["L"], a["Hq"], a["Hkv"],
+                                 a["d"], a["G"], a["sh"], ctypes.byref(opts), ws, ws_bytes, None)
+
+
+def bwd_ex(opts, ws=None, ws_bytes=0, **kw):
+    a = dict(GOOD, **kw)
+    return L.lib().s2attn_bwd_ex(*([FAKE] * 9), a["B"], a["L"], a["Hq"], a["Hkv"], a["d"], a["G"],
+                                 a["sh"], ctypes.byref(opts), ws, ws_bytes, None)
+
+
+INV, UNS, WS = L.S2ATTN_ERR_INVALID_ARG, L.S2ATTN_ERR_UNSUPPORTED, L.S2ATTN_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=None), INV), (dict(k=None), INV), (dict(v=None), INV), (dict(o=None), INV),
+    (dict(lse=None), INV), (dict(q=MIS), INV), (dict(lse=MIS), INV),
+    (dict(B=0), INV), (dict(L=0), INV), (dict(Hq=-1), INV), (dict(Hkv=0), INV), (dict(d=0), INV),
+    (dict(G=0), INV), (dict(G=48), INV),                   # L % G != 0
+    (dict(Hkv=3), INV),                                    # Hq % Hkv != 0
+    (dict(sh=-1), INV), (dict(sh=5), INV),                 # shifted_heads outside [0, Hq]
+    (dict(L=255, G=51, sh=1), INV),                        # odd G with shifted heads
+    (dict(d=96), UNS), (dict(d=32), UNS),
+])
+def test_fwd_argument_checks(kw, want):
+    assert fwd(**kw) == want
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(do=None), INV), (dict(dq=None), INV), (dict(dk=None), INV), (dict(dv=None), INV),
+    (dict(delta=None), INV), (dict(dv=MIS), INV), (dict(delta=MIS), INV),
+    (dict(G=100), INV), (dict(d=80), UNS),
+    (dict(Hq=8, Hkv=2, sh=3), UNS),   # a KV head shared by shifted and unshifted query heads
+])
+def test_bwd_argument_checks(kw, want):
+    assert bwd(**kw) == want
+
+
+def test_opts_checks():
+    o = s2.s2attn_opts_init()
+    o.struct_size = 4
+    assert fwd_ex(o) == INV
+    o = s2.s2attn_opts_init()
+    o.dtype = 7
+    assert fwd_ex(o) == INV
+    o = s2.s2attn_opts_init()
+    o.grad_dtype = -1
+    assert bwd_ex(o) == INV
+    o = s2.s2attn_opts_init()
+    o.softmax_scale = float("nan")
+    assert fwd_ex(o) == INV
+    o = s2.s2attn_opts_init()
+    o.rope, o.rope_base = 1, 0.5
+    assert fwd_ex(o) == INV
+    o = s2.s2attn_opts_init()
+    o.rope, o.rope_orig_len = 1, 0
+    assert fwd_ex(o) == INV
+    o = s2.s2attn_opts_init()
+    o.dtype, o.rope = L.S2ATTN_F32, 1
+    assert fwd_ex(o) == UNS                          # RoPE needs bf16 inputs
+    o = s2.s2attn_opts_init()
+    o.dtype, o.grad_dtype = L.S2ATTN_F32, L.S2ATTN_BF16
+    assert bwd_ex(o) == UNS
+
+
+def test_workspace_sizes_and_checks():
+    o = s2.s2attn_opts_init()
+    B, Ln, Hq, Hkv, d, G = 1, 256, 4, 2, 64, 64
+    assert s2.s2attn_workspace_size(0, B, Ln, Hq, Hkv, d, G, o) == 0
+    delta = B * Hq * Ln * 4
+    assert s2.s2attn_workspace_size(1, B, Ln, Hq, Hkv, d, G, o) == (delta + 255) // 256 * 256
+    o.rope = 1
+    rq, rk = B * Ln * Hq * d * 2, B * Ln * Hkv * d * 2
+    r256 = lambda x: (x + 255) // 256 * 256
+    assert s2.s2attn_workspace_size(0, B, Ln, Hq, Hkv, d, G, o) == r256(rq) + r256(rk)
+    assert s2.s2attn_workspace_size(1, B, Ln, Hq, Hkv, d, G, o) == r256(delta) + r256(rq) + r256(rk)
+    assert s2.s2attn_workspace_size(0, 0, Ln, Hq, Hkv, d, G, o) == 0   # invalid sizes -> 0
+    # missing / short workspace
+    need = s2.s2attn_workspace_size(0, B, Ln, Hq, Hkv, d, G, o)
+    assert fwd_ex(o, None, 0, Hkv=2) == WS
+    assert fwd_ex(o, FAKE, need - 1, Hkv=2) == WS
+    assert fwd_ex(o, MIS, need, Hkv=2) == WS
+    o2 = s2.s2attn_opts_init()
+    assert bwd_ex(o2, None, 0, Hkv=2) == WS          # the backward always needs delta space
+
+
+def test_python_wrappers_raise_named_errors():
+    with pytest.raises(s2.S2AttnError) as e:
+        s2.s2attn_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 256, 4, 4, 64, 60, 0)
+    assert e.value.status == INV and "INVALID_ARG" in str(e.value)
+
+
+def test_header_documents_each_entry_point():
+    src = open(HEADER).read()
+    for name in declared_functions():
+        i = src.index(name + "(")
+        before = src[max(0, i - 600):i]
+        assert "/*" in before, f"{name} lacks a comment"

@@ -1,0 +1,337 @@
+"""GPU parity: libs2attn's HIP kernels against the CPU oracle on seeded inputs.
+
+Small shapes (several tiles, ragged tails, GQA, RoPE, degenerate groups) are
+compared element by element over whole tensors.  The five workloads run at
+full size on the GPU and are compared on the units (one KV head and group,
+with all its query heads) that the oracle recomputes one by one, plus
+properties that hold at any size over every group.
+
+Tolerances: bf16 outputs and gradients rel-Frobenius <= 5e-3 and max-abs <=
+2e-2; fp32 path <= 1e-5 for both.  Where a gradient's magnitude puts half a
+bf16 ulp above 2e-2 (dK, dV of the grouped-query workload reach ~10), parity
+is judged on fp32-stored gradients of the same kernels, and the bf16-stored
+result is held to its rounding floor instead.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import shifted_sparse_attention_amd as s2
+from oracle import s2attn as O
+from seeded_inputs import CONFIGS, make_inputs
+from seeded_inputs.gen import bf16_round
+from tests.gpu_util import (BF16_MAX_ABS, BF16_REL_F, F32_TOL, bf16_store_tol, check, dev,
+                            host, say)
+
+pytestmark = pytest.mark.gpu
+
+BF = torch.bfloat16
+
+
+def rand_inputs(seed, B, L, Hq, Hkv, d, bf16=True):
+    rng = np.random.default_rng(seed)
+    out = []
+    for shp in ((B, L, Hq, d), (B, L, Hkv, d), (B, L, Hkv, d), (B, L, Hq, d)):
+        x = rng.standard_normal(shp, dtype=np.float32)
+        out.append(bf16_round(x) if bf16 else x)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Small shapes, whole tensors.
+# ---------------------------------------------------------------------------
+
+SMALL = [
+    # B, L, Hq, Hkv, d, G, shifted, rope
+    (1, 256, 4, 4, 64, 64, 2, None),
+    (2, 640, 4, 2, 128, 320, 2, None),       # q tiles 128+128+64 (ragged), GQA r=2, B=2
+    (1, 600, 2, 1, 128, 200, 2, None),       # G not a multiple of 64, MQA
+    (1, 512, 4, 4, 128, 512, 0, None),       # G = L, no shift: full causal attention
+    (1, 1024, 8, 1, 64, 256, 8, None),       # every head shifted, r=8
+    (1, 64, 2, 2, 128, 2, 2, None),          # tiny groups
+    (1, 64, 2, 2, 64, 1, 0, None),           # G = 1: o = v
+    (1, 1536, 2, 2, 128, 768, 1, (10000.0, 256)),  # RoPE with position interpolation
+    (1, 768, 4, 2, 64, 384, 2, (500.0, 64)),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[f"B{c[0]}L{c[1]}H{c[2]}/{c[3]}d{c[4]}G{c[5]}s{c[6]}"
+                                             f"{'rope' if c[7] else ''}" for c in SMALL])
+def test_small_bf16_fwd_bwd(case):
+    B, L, Hq, Hkv, d, G, sh, rope = case
+    say(f"[small bf16] {case}")
+    q, k, v, do = rand_inputs(1000 + L + G, B, L, Hq, Hkv, d)
+    tq, tk, tv, tdo = (dev(x, BF) for x in (q, k, v, do))
+    o, lse = s2.forward(tq, tk, tv, G, sh, rope=rope)
+    g32 = s2.backward(tq, tk, tv, o, lse, tdo, G, sh, rope=rope, grad_dtype=torch.float32)
+    g16 = s2.backward(tq, tk, tv, o, lse, tdo, G, sh, rope=rope)
+    torch.cuda.synchronize()
+    rdq, rdk, rdv, ro, rlse = O.backward(q, k, v, do, G, sh, rope=rope)
+    check("o", host(o), ro, BF16_REL_F, bf16_store_tol(ro))
+    check("lse", host(lse), rlse, BF16_REL_F, BF16_MAX_ABS)
+    for name, a, b, ref in zip(("dq", "dk", "dv"), g32, g16, (rdq, rdk, rdv)):
+        check(name, host(a), ref, BF16_REL_F, BF16_MAX_ABS)
+        check(name + "(bf16)", host(b), ref, BF16_REL_F, bf16_store_tol(ref))
+
+
+F32_CASES = [
+    (1, 256, 4, 2, 64, 64, 2),
+    (1, 192, 2, 2, 128, 96, 1),
+    (2, 120, 2, 1, 64, 40, 0),
+]
+
+
+@pytest.mark.parametrize("case", F32_CASES)
+def test_small_f32_fwd_bwd(case):
+    B, L, Hq, Hkv, d, G, sh = case
+    say(f"[small f32] {case}")
+    q, k, v, do = rand_inputs(2000 + L, B, L, Hq, Hkv, d, bf16=False)
+    tq, tk, tv, tdo = (dev(x, torch.float32) for x in (q, k, v, do))
+    o, lse = s2.forward(tq, tk, tv, G, sh)
+    dq, dk, dv = s2.backward(tq, tk, tv, o, lse, tdo, G, sh)
+    torch.cuda.synchronize()
+    rdq, rdk, rdv, ro, rlse = O.backward(q, k, v, do, G, sh)
+    for name, x, r in (("o", o, ro), ("lse", lse, rlse), ("dq", dq, rdq), ("dk", dk, rdk),
+                       ("dv", dv, rdv)):
+        check(name, host(x), r, F32_TOL, F32_TOL)
+
+
+# ---------------------------------------------------------------------------
+# The five workloads at full size.
+# ---------------------------------------------------------------------------
+
+def test_workload_fwd_f32_L256():
+    wl = CONFIGS["fwd_f32_L256"]
+    say(f"[workload] {wl.name}")
+    x = make_inputs(wl)
+    tq, tk, tv = (dev(x[n], torch.float32) for n in ("q", "k", "v"))
+    o, lse = s2.forward(tq, tk, tv, wl.G, wl.shifted_heads)
+    torch.cuda.synchronize()
+    ro, rlse = O.forward(x["q"], x["k"], x["v"], wl.G, wl.shifted_heads)
+    check("o", host(o), ro, F32_TOL, F32_TOL)
+    check("lse", host(lse), rlse, F32_TOL, F32_TOL)
+
+
+def test_workload_fwd_bf16_L8k():
+    wl = CONFIGS["fwd_bf16_L8k"]
+    say(f"[workload] {wl.name}")
+    x = make_inputs(wl)
+    tq, tk, tv = (dev(x[n], BF) for n in ("q", "k", "v"))
+    o, lse = s2.forward(tq, tk, tv, wl.G, wl.shifted_heads)
+    torch.cuda.synchronize()
+    ro, rlse = O.forward(x["q"], x["k"], x["v"], wl.G, wl.shifted_heads)
+    check("o", host(o), ro, BF16_REL_F, BF16_MAX_ABS)
+    check("lse", host(lse), rlse, BF16_REL_F, BF16_MAX_ABS)
+
+
+def _group_sums_hold(wl, tdo, dk, dv, rope):
+    """Over every KV head and group: sum_j dV_j = sum over its query heads of sum_i dO_i,
+    and (without RoPE) sum_j dK_j = 0."""
+    B, L, Hq, Hkv, G, r = wl.B, wl.L, wl.Hq, wl.Hkv, wl.G, wl.r
+    worst_v, worst_k = 0.0, 0.0
+    do64, dv64, dk64 = tdo.double(), dv.double(), dk.double()
+    for hk in range(Hkv):
+        s = O.head_shift(hk * r, Hq, G, wl.shifted_heads)
+        for g in range(L // G):
+            rows = torch.from_numpy(O.group_members(L, G, s, g)).cuda()
+            want = do64[:, rows, hk * r:(hk + 1) * r].sum(dim=(1, 2))
+            got = dv64[:, rows, hk].sum(dim=1)
+            worst_v = max(worst_v, float((got - want).abs().max() / (want.abs().max() + 1)))
+            if not rope:
+                worst_k = max(worst_k, float(dk64[:, rows, hk].sum(dim=1).abs().max()))
+    say(f"  group sums: dV vs dO rel {worst_v:.2e}; |sum dK| {worst_k:.2e}")
+    assert worst_v < 2e-2
+    if not rope:
+        assert worst_k < 0.5   # a sum of G bf16 values of size ~1 that cancels exactly
+
+
+def _sampled_parity(wl, x, outs, kv_units, grads_f32, o_lse=True):
+    o, lse, dq, dk, dv = outs
+    rope = (wl.rope_base, wl.rope_orig_len) if wl.rope else None
+    res = O.sampled_kv_backward(x["q"], x["k"], x["v"], x["do"], wl.G, wl.shifted_heads,
+                                kv_units, rope=rope)
+    gtol = (BF16_REL_F, BF16_MAX_ABS)
+    for (b, hk, g), r in res.items():
+        rows = torch.from_numpy(r["rows"]).cuda()
+        say(f" unit b={b} kv_head={hk} group={g}")
+        heads = sorted(r["dq"])
+        if o_lse:
+            check("o", np.stack([host(o[b, rows, h]) for h in heads]),
+                  np.stack([r["o"][h] for h in heads]), BF16_REL_F, BF16_MAX_ABS)
+            check("lse", np.stack([host(lse[b, h, rows]) for h in heads]),
+                  np.stack([r["lse"][h] for h in heads]), BF16_REL_F, BF16_MAX_ABS)
+        rdq = np.stack([r["dq"][h] for h in heads])
+        gdq = np.stack([host(dq[b, rows, h]) for h in heads])
+        for name, got, ref in (("dq", gdq, rdq), ("dk", host(dk[b, rows, hk]), r["dk"]),
+                               ("dv", host(dv[b, rows, hk]), r["dv"])):
+            if grads_f32:
+                check(name, got, ref, *gtol)
+            else:
+                # bf16-stored: the tolerance plus the store's own rounding
+                check(name + "(bf16)", got, ref, BF16_REL_F, bf16_store_tol(ref))
+
+
+def _run_fwdbwd(wl, x, grad_dtype=BF):
+    rope = (wl.rope_base, wl.rope_orig_len) if wl.rope else None
+    tq, tk, tv, tdo = (dev(x[n], BF) for n in ("q", "k", "v", "do"))
+    o, lse = s2.forward(tq, tk, tv, wl.G, wl.shifted_heads, rope=rope)
+    dq, dk, dv = s2.backward(tq, tk, tv, o, lse, tdo, wl.G, wl.shifted_heads, rope=rope,
+                             grad_dtype=grad_dtype)
+    torch.cuda.synchronize()
+    return (tq, tk, tv, tdo), (o, lse, dq, dk, dv)
+
+
+def test_workload_fwdbwd_bf16_L32k():
+    wl = CONFIGS["fwdbwd_bf16_L32k"]
+    say(f"[workload] {wl.name}")
+    x = make_inputs(wl)
+    # unshifted head / first group, shifted head / last group (holds the wrap), one in between
+    units = [(0, 0, 0), (0, 31, 3), (0, 20, 1)]
+    ins, outs = _run_fwdbwd(wl, x, grad_dtype=torch.float32)
+    _group_sums_hold(wl, ins[3], outs[3], outs[4], rope=False)
+    say(" gradients stored in fp32")
+    _sampled_parity(wl, x, outs, units, grads_f32=True)
+    del outs
+    _, outs16 = _run_fwdbwd(wl, x, grad_dtype=BF)
+    say(" gradients stored in bf16")
+    _group_sums_hold(wl, ins[3], outs16[3], outs16[4], rope=False)
+    _sampled_parity(wl, x, outs16, units[:2], grads_f32=False, o_lse=False)
+
+
+def test_workload_fwdbwd_bf16_L100k_rope():
+    wl = CONFIGS["fwdbwd_bf16_L100k_rope"]
+    say(f"[workload] {wl.name}")
+    x = make_inputs(wl)
+    units = [(0, 31, 3)]
+    ins, outs = _run_fwdbwd(wl, x, grad_dtype=torch.float32)
+    _group_sums_hold(wl, ins[3], outs[3], outs[4], rope=True)
+    say(" gradients stored in fp32")
+    _sampled_parity(wl, x, outs, units, grads_f32=True)
+    # forward of an unshifted unit as well
+    fw = O.sampled_forward(x["q"], x["k"], x["v"], wl.G, wl.shifted_heads, [(0, 0, 1)],
+                           rope=(wl.rope_base, wl.rope_orig_len))
+    for (b, h, g), (rows, ro, rl) in fw.items():
+        tr = torch.from_numpy(rows).cuda()
+        check("o[h0]", host(outs[0][b, tr, h]), ro, BF16_REL_F, BF16_MAX_ABS)
+        check("lse[h0]", host(outs[1][b, h, tr]), rl, BF16_REL_F, BF16_MAX_ABS)
+    del outs
+    _, outs16 = _run_fwdbwd(wl, x, grad_dtype=BF)
+    say(" gradients stored in bf16")
+    _sampled_parity(wl, x, outs16, units, grads_f32=False, o_lse=False)
+
+
+def test_workload_fwdbwd_bf16_L32k_gqa():
+    wl = CONFIGS["fwdbwd_bf16_L32k_gqa"]
+    say(f"[workload] {wl.name}")
+    x = make_inputs(wl)
+    ins, outs32 = _run_fwdbwd(wl, x, grad_dtype=torch.float32)
+    _group_sums_hold(wl, ins[3], outs32[3], outs32[4], rope=False)
+    units = [(0, 0, 0), (0, 7, 3)]
+    say(" gradients stored in fp32")
+    _sampled_parity(wl, x, outs32, units, grads_f32=True)
+    del outs32
+    _, outs16 = _run_fwdbwd(wl, x, grad_dtype=BF)
+    say(" gradients stored in bf16")
+    _sampled_parity(wl, x, outs16, units[1:], grads_f32=False, o_lse=False)
+
+
+# ---------------------------------------------------------------------------
+# Kernel-level invariants.
+# ---------------------------------------------------------------------------
+
+INV_SHAPE = dict(B=1, L=2048, Hq=4, Hkv=4, d=128, G=512, sh=2)
+
+
+def _inv_inputs(seed=7):
+    s = INV_SHAPE
+    return rand_inputs(seed, s["B"], s["L"], s["Hq"], s["Hkv"], s["d"])
+
+
+def _all_outputs(q, k, v, do, grad_dtype=BF):
+    s = INV_SHAPE
+    tq, tk, tv, tdo = (dev(x, BF) for x in (q, k, v, do))
+    o, lse = s2.forward(tq, tk, tv, s["G"], s["sh"])
+    dq, dk, dv = s2.backward(tq, tk, tv, o, lse, tdo, s["G"], s["sh"], grad_dtype=grad_dtype)
+    torch.cuda.synchronize()
+    return [t.cpu() for t in (o, lse, dq, dk, dv)]
+
+
+def test_run_to_run_bit_determinism():
+    say("[invariant] determinism")
+    x = _inv_inputs()
+    a, b = _all_outputs(*x), _all_outputs(*x)
+    for u, w in zip(a, b):
+        assert torch.equal(u, w)
+
+
+def test_group_independence_bitwise():
+    say("[invariant] group independence")
+    s = INV_SHAPE
+    q, k, v, do = _inv_inputs(8)
+    base = _all_outputs(q, k, v, do)
+    h, g = 3, 1   # a shifted head
+    rows = O.unit_rows(s["L"], s["G"], s["Hq"], s["sh"], h, g)
+    rng = np.random.default_rng(9)
+    q2, k2, v2, do2 = (x.copy() for x in (q, k, v, do))
+    for x in (q2, k2, v2, do2):
+        x[0, rows, h] = bf16_round(rng.standard_normal((len(rows), s["d"]), dtype=np.float32))
+    pert = _all_outputs(q2, k2, v2, do2)
+    other = torch.from_numpy(np.setdiff1d(np.arange(s["L"]), rows))
+    rows_t = torch.from_numpy(rows)
+    for name, a, b in zip(("o", "lse", "dq", "dk", "dv"), base, pert):
+        if name == "lse":
+            assert torch.equal(a[0, h, other], b[0, h, other]), name
+            assert not torch.equal(a[0, h, rows_t], b[0, h, rows_t]), name
+            assert torch.equal(a[0, :h], b[0, :h]), name
+        else:
+            assert torch.equal(a[0, other, h], b[0, other, h]), name
+            assert not torch.equal(a[0, rows_t, h], b[0, rows_t, h]), name
+            assert torch.equal(a[0, :, :h], b[0, :, :h]), name
+
+
+def test_roll_by_group_equivariance_bitwise():
+    say("[invariant] roll by G")
+    s = INV_SHAPE
+    x = _inv_inputs(10)
+    a = _all_outputs(*x)
+    b = _all_outputs(*(np.roll(t, s["G"], axis=1) for t in x))
+    for name, u, w in zip(("o", "lse", "dq", "dk", "dv"), a, b):
+        ax = 2 if name == "lse" else 1
+        assert torch.equal(torch.roll(u, s["G"], dims=ax), w), name
+
+
+def test_every_output_written_and_no_stray_writes():
+    """Outputs pre-filled with NaN come back finite; sentinels around every
+    output buffer are untouched."""
+    say("[invariant] nan-fill and redzones")
+    s = INV_SHAPE
+    q, k, v, do = _inv_inputs(11)
+    B, L, Hq, Hkv, d, G, sh = s["B"], s["L"], s["Hq"], s["Hkv"], s["d"], s["G"], s["sh"]
+    tq, tk, tv, tdo = (dev(x, BF) for x in (q, k, v, do))
+    pad = 4096
+    SENT = -1024.0   # exact in bf16 and fp32
+
+    def padded(n, dtype):
+        buf = torch.full((n + 2 * pad,), SENT, dtype=dtype, device="cuda")
+        body = buf[pad:pad + n]
+        body.fill_(float("nan"))
+        return buf, body
+
+    nq, nk, nl = B * L * Hq * d, B * L * Hkv * d, B * Hq * L
+    ob, o = padded(nq, BF)
+    lb, lse = padded(nl, torch.float32)
+    s2.s2attn_fwd(tq, tk, tv, o, lse, B, L, Hq, Hkv, d, G, sh)
+    dqb, dq = padded(nq, BF)
+    dkb, dk = padded(nk, BF)
+    dvb, dv = padded(nk, BF)
+    deb, de = padded(nl, torch.float32)
+    s2.s2attn_bwd(tq, tk, tv, o, lse, tdo, dq, dk, dv, de, B, L, Hq, Hkv, d, G, sh)
+    torch.cuda.synchronize()
+    for buf, body in ((ob, o), (lb, lse), (dqb, dq), (dkb, dk), (dvb, dv), (deb, de)):
+        assert torch.isfinite(body.float()).all()
+        assert (buf[:pad].float() == SENT).all() and (buf[-pad:].float() == SENT).all()
+    # and the values are right
+    rdq, rdk, rdv, ro, rl = O.backward(q, k, v, do, G, sh)
+    check("o", host(o.view(B, L, Hq, d)), ro, BF16_REL_F, BF16_MAX_ABS)
+    check("dk", host(dk.view(B, L, Hkv, d)), rdk, BF16_REL_F, BF16_MAX_ABS)
