@@ -1,0 +1,217 @@
+"""Throughput of S2-Attn forward + backward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the whole path over one batch of synthetic inputs
+already resident in HBM: the forward (O, LSE) and the backward (row term,
+dK/dV, dQ).  The default workload is Llama2-7B heads at 32k context
+(B=1, Hq=Hkv=32, d=128, L=32768, G=8192, 16 heads shifted), seeded N(0, 1)
+inputs rounded to bf16.  Throughput counts group-local causal FLOPs
+(forward 2*B*Hq*L*G*d, backward 2.5x that).
+
+Printed: one JSON line with the throughput, the roofline of the dominant
+kernel (its average duration from HIP events recorded on its launch stream
+inside the timed region) and the CPU oracle timed on a bounded sample.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "S²-Attn fwd+bwd TFLOP/s and % of bf16 MFMA peak, Llama2-7B heads, L=32k"
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CUs x 2.4 GHz x 4096 FLOP/clk
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwdbwd_bf16_L32k.json")
+
+
+def kernel_source_sha():
+    """Hash of the kernel sources, to tell whether stored counters are current."""
+    csrc = os.path.join(ROOT, "shifted_sparse_attention_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h", ".cpp")):
+            h.update(f.encode())
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="after timing, run one device copy of this many MiB (counter calibration)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(this build runs on a single GPU; units are independent, so several GPUs would "
+              "split heads or batch with no exchange)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import shifted_sparse_attention_amd as s2
+    from seeded_inputs import CONFIGS, make_inputs
+    from seeded_inputs.configs import HEADLINE
+    from shifted_sparse_attention_amd import flops as F
+
+    wl = CONFIGS[args.workload or HEADLINE]
+    if wl.dtype != "bf16" or not wl.backward:
+        raise SystemExit("bench.py times bf16 forward+backward workloads")
+    B, L, Hq, Hkv, d, G, sh = wl.B, wl.L, wl.Hq, wl.Hkv, wl.d, wl.G, wl.shifted_heads
+    rope = (wl.rope_base, wl.rope_orig_len) if wl.rope else None
+
+    t0 = time.time()
+    x = make_inputs(wl)
+    dev = torch.device("cuda:0")
+    tq, tk, tv, tdo = (torch.from_numpy(x[n]).to(torch.bfloat16).to(dev) for n in ("q", "k", "v", "do"))
+    print(f"# inputs ready in {time.time() - t0:.1f}s: {wl.name}", file=sys.stderr, flush=True)
+
+    o = torch.empty_like(tq)
+    lse = torch.empty((B, Hq, L), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(tq), torch.empty_like(tk), torch.empty_like(tv)
+    opts = s2.make_opts(torch.bfloat16, rope=rope)
+    fws = s2.s2attn_workspace_size(0, B, L, Hq, Hkv, d, G, opts)
+    bws = s2.s2attn_workspace_size(1, B, L, Hq, Hkv, d, G, opts)
+    ws = torch.empty(max(fws, bws, 256), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    sargs = (tq, tk, tv, o, lse, tdo, dq, dk, dv, B, L, Hq, Hkv, d, G, sh, opts, ws, bws, stream)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        s2.s2attn_fwd_ex(tq, tk, tv, o, lse, B, L, Hq, Hkv, d, G, sh, opts, ws, fws, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        s2.s2attn_bwd_stage_ex(s2.S2ATTN_BWD_STAGE_PRE, *sargs)
+        if ev is not None:
+            ev[2].record(stream)
+        s2.s2attn_bwd_stage_ex(s2.S2ATTN_BWD_STAGE_DKDV, *sargs)
+        if ev is not None:
+            ev[3].record(stream)
+        s2.s2attn_bwd_stage_ex(s2.S2ATTN_BWD_STAGE_DQ, *sargs)
+        if ev is not None:
+            ev[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / args.steps
+    names = ["fwd", "bwd_pre", "bwd_dkdv", "bwd_dq"]
+    kms = {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, n in enumerate(names)}
+
+    if args.copy_probe_mb:
+        n = args.copy_probe_mb * (1 << 20)
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b = torch.empty(n, dtype=torch.uint8, device=dev)
+        b.copy_(a)
+        torch.cuda.synchronize()
+
+    fl = F.fwd_bwd_flops(B, L, Hq, d, G)
+    tflops = fl / (ms_step * 1e-3) / 1e12
+    unit = float(B) * Hq * L * G * d     # one product over all group-local causal pairs
+    alg_flops = {"fwd": 2 * unit, "bwd_dkdv": 4 * unit, "bwd_dq": 1 * unit}
+    dom = max(alg_flops, key=lambda n: kms[n])
+    achieved = alg_flops[dom] / (kms[dom] * 1e-3) / 1e12
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        tr = json.load(open(TRAFFIC_FILE))
+        if tr.get("source_sha") == kernel_source_sha() and dom in tr.get("kernels", {}):
+            traffic = tr["kernels"][dom]["hbm_bytes_per_launch"]
+
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": B, "L": L, "Hq": Hq, "Hkv": Hkv, "d": d, "G": G,
+                   "shifted_heads": sh, "rope": bool(wl.rope), "seed": wl.seed,
+                   "parallelism": "single GPU"},
+        "pct_of_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "kernels_ms": {k: round(v, 4) for k, v in kms.items()},
+        "roofline": {
+            "kernel": dom,
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+            "algorithmic_flops_per_launch": alg_flops[dom],
+        },
+    }
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(wl, x, seconds):
+    """The oracle (fp64 numpy, as it stands) on whole (head, group) units of the
+    same workload, forward + backward, until about `seconds` of CPU time."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import s2attn as O
+    from shifted_sparse_attention_amd import flops as F
+
+    scale = 1.0 / np.sqrt(wl.d)
+    units = [(0, h, g) for g in range(wl.n_groups) for h in (0, wl.Hq - 1, wl.Hq // 2, 1)]
+    done, t0 = 0, time.time()
+    for b, h, g in units:
+        rows = O.unit_rows(wl.L, wl.G, wl.Hq, wl.shifted_heads, h, g)
+        hk = h // wl.r
+        O.unit_backward(x["q"][b, rows, h].astype(np.float64), x["k"][b, rows, hk].astype(np.float64),
+                        x["v"][b, rows, hk].astype(np.float64), x["do"][b, rows, h].astype(np.float64),
+                        scale)
+        done += 1
+        if time.time() - t0 >= seconds:
+            break
+    dt = time.time() - t0
+    fl = done * F.fwd_bwd_flops(1, wl.G, 1, wl.d, wl.G)   # one unit = one head, one group
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                   if i.get("user_api") == "blas"] or [1])
+    return {"value": round(fl / dt / 1e12, 5), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} (head, group) units of G={wl.G} rows, forward+backward in fp64 "
+                      f"({dt:.1f} s); counted FLOPs as for the GPU",
+            "seconds": round(dt, 2)}
+
+
+if __name__ == "__main__":
+    main()

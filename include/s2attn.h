@@ -49,10 +49,10 @@ typedef enum {
     S2ATTN_ERR_INVALID_ARG = 1,  /* null pointer, size <= 0, L % G != 0, odd G with shifted
                                     heads, Hq % Hkv != 0, shifted_heads outside [0, Hq],
                                     bad opts (struct_size, dtype, rope fields) */
-    S2ATTN_ERR_UNSUPPORTED = 2,  /* d not in {64, 128}; shifted_heads % (Hq/Hkv) != 0 (a KV
-                                    head shared by shifted and unshifted query heads); bf16
-                                    path with G % 128 != 0 or (shifted) G/2 % 64 != 0;
-                                    RoPE with float32 inputs */
+    S2ATTN_ERR_UNSUPPORTED = 2,  /* d not in {64, 128}; backward with shifted_heads % (Hq/Hkv)
+                                    != 0 (a KV head shared by shifted and unshifted query
+                                    heads); RoPE with float32 inputs; bf16 gradients of
+                                    float32 inputs; sizes whose grid exceeds 2^31 blocks */
     S2ATTN_ERR_WORKSPACE = 3,    /* workspace missing or smaller than s2attn_workspace_size() */
     S2ATTN_ERR_HIP = 4           /* a HIP runtime error (no device, launch failure, ...) */
 } s2attn_status;
@@ -61,6 +61,13 @@ typedef enum {
     S2ATTN_BF16 = 0,
     S2ATTN_F32 = 1
 } s2attn_dtype;
+
+/* Stages of the backward, for s2attn_bwd_stage_ex. */
+enum {
+    S2ATTN_BWD_STAGE_PRE = 0,
+    S2ATTN_BWD_STAGE_DKDV = 1,
+    S2ATTN_BWD_STAGE_DQ = 2
+};
 
 /*
  * Options for the _ex entry points.  Fill with s2attn_opts_init() first.
@@ -127,6 +134,22 @@ int s2attn_bwd_ex(const void* q, const void* k, const void* v, const void* o,
                   const float* lse, const void* dout, void* dq, void* dk, void* dv,
                   int B, int L, int Hq, int Hkv, int d, int G, int shifted_heads,
                   const s2attn_opts* opts, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * The backward as its three kernels, for callers that time or overlap them.
+ * Arguments are those of s2attn_bwd_ex, with the same workspace.
+ *   S2ATTN_BWD_STAGE_PRE   delta = rowsum(dout * o) into the workspace (and,
+ *                          with RoPE, the rotated q and k).
+ *   S2ATTN_BWD_STAGE_DKDV  dk, dv.  Needs PRE complete.
+ *   S2ATTN_BWD_STAGE_DQ    dq.  Needs PRE complete.
+ * PRE, DKDV, DQ in that order on one stream equal s2attn_bwd_ex; DKDV and DQ
+ * read only PRE's results and the inputs, so they may run concurrently on two
+ * streams once PRE has finished.  Any other stage value: S2ATTN_ERR_INVALID_ARG.
+ */
+int s2attn_bwd_stage_ex(int stage, const void* q, const void* k, const void* v, const void* o,
+                        const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                        int B, int L, int Hq, int Hkv, int d, int G, int shifted_heads,
+                        const s2attn_opts* opts, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Static string naming a status code. */
 const char* s2attn_status_string(int status);

@@ -23,6 +23,10 @@ S2ATTN_ERR_HIP = 4
 S2ATTN_BF16 = 0
 S2ATTN_F32 = 1
 
+S2ATTN_BWD_STAGE_PRE = 0
+S2ATTN_BWD_STAGE_DKDV = 1
+S2ATTN_BWD_STAGE_DQ = 2
+
 
 class S2AttnError(RuntimeError):
     def __init__(self, status, what):
@@ -52,6 +56,8 @@ _SIGS = {
     "s2attn_workspace_size": (_sz, [_ci] * 7 + [ctypes.POINTER(s2attn_opts)]),
     "s2attn_fwd_ex": (_ci, [_vp] * 5 + [_ci] * 7 + [ctypes.POINTER(s2attn_opts), _vp, _sz, _vp]),
     "s2attn_bwd_ex": (_ci, [_vp] * 9 + [_ci] * 7 + [ctypes.POINTER(s2attn_opts), _vp, _sz, _vp]),
+    "s2attn_bwd_stage_ex": (_ci, [_ci] + [_vp] * 9 + [_ci] * 7
+                            + [ctypes.POINTER(s2attn_opts), _vp, _sz, _vp]),
     "s2attn_status_string": (ctypes.c_char_p, [_ci]),
     "s2attn_version": (_ci, []),
 }
@@ -153,6 +159,14 @@ def s2attn_bwd_ex(q, k, v, o, lse, dout, dq, dk, dv, B, L, Hq, Hkv, d, G, shifte
                                _ptr(dq), _ptr(dk), _ptr(dv), B, L, Hq, Hkv, d, G, shifted_heads,
                                _opts_ptr(opts), _ptr(ws), int(ws_bytes), _stream(stream)),
            "s2attn_bwd_ex")
+
+
+def s2attn_bwd_stage_ex(stage, q, k, v, o, lse, dout, dq, dk, dv, B, L, Hq, Hkv, d, G,
+                        shifted_heads, opts, ws, ws_bytes, stream=None):
+    _check(lib().s2attn_bwd_stage_ex(int(stage), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                     _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), B, L, Hq, Hkv, d,
+                                     G, shifted_heads, _opts_ptr(opts), _ptr(ws), int(ws_bytes),
+                                     _stream(stream)), f"s2attn_bwd_stage_ex({stage})")
 
 
 def s2attn_status_string(status):

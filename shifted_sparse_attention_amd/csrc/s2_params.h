@@ -51,8 +51,10 @@ __host__ __device__ inline size_t lse_idx(const Params& p, int b, int h, int t) 
 hipError_t launch_fwd_bf16(const Params& p, hipStream_t s);
 hipError_t launch_fwd_f32(const Params& p, hipStream_t s);
 hipError_t launch_bwd_pre(const Params& p, int f32_io, hipStream_t s);
-hipError_t launch_bwd_bf16(const Params& p, int grad_f32, hipStream_t s);
-hipError_t launch_bwd_f32(const Params& p, hipStream_t s);
+hipError_t launch_bwd_dkdv_bf16(const Params& p, int grad_f32, hipStream_t s);
+hipError_t launch_bwd_dq_bf16(const Params& p, int grad_f32, hipStream_t s);
+hipError_t launch_bwd_dkdv_f32(const Params& p, hipStream_t s);
+hipError_t launch_bwd_dq_f32(const Params& p, hipStream_t s);
 hipError_t launch_rope_prepass(const Params& p, void* q_out, void* k_out, hipStream_t s);
 
 }  // namespace s2

@@ -155,10 +155,12 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
     return hip_status(s2::launch_fwd_bf16(p, stream));
 }
 
+constexpr int kStagePre = 1, kStageDkdv = 2, kStageDq = 4, kStageAll = 7;
+
 int bwd_impl(const void* q, const void* k, const void* v, const void* o, const float* lse,
              const void* dout, void* dq, void* dk, void* dv, float* delta, int B, int L, int Hq,
              int Hkv, int d, int G, int shifted_heads, const s2attn_opts* opts, void* ws,
-             size_t ws_bytes, hipStream_t stream) {
+             size_t ws_bytes, hipStream_t stream, int stages) {
     if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return S2ATTN_ERR_INVALID_ARG;
     const void* ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv};
     for (const void* ptr : ptrs)
@@ -193,18 +195,30 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const f
     p.dv = dv;
     p.delta = delta;
 
-    hipError_t e = s2::launch_bwd_pre(p, r.dtype == S2ATTN_F32, stream);
-    if (e != hipSuccess) return S2ATTN_ERR_HIP;
-    if (r.dtype == S2ATTN_F32) return hip_status(s2::launch_bwd_f32(p, stream));
+    char* rq = base + wl.rq_off;
+    char* rk = base + wl.rk_off;
+    if (stages & kStagePre) {
+        if (s2::launch_bwd_pre(p, r.dtype == S2ATTN_F32, stream) != hipSuccess)
+            return S2ATTN_ERR_HIP;
+        if (r.rope && s2::launch_rope_prepass(p, rq, rk, stream) != hipSuccess)
+            return S2ATTN_ERR_HIP;
+    }
     if (r.rope) {
-        void* rq = base + wl.rq_off;
-        void* rk = base + wl.rk_off;
-        e = s2::launch_rope_prepass(p, rq, rk, stream);
-        if (e != hipSuccess) return S2ATTN_ERR_HIP;
         p.q = rq;
         p.k = rk;  // p.rope stays set: the epilogues rotate dq, dk back
     }
-    return hip_status(s2::launch_bwd_bf16(p, r.grad_dtype == S2ATTN_F32, stream));
+    const int gf = r.grad_dtype == S2ATTN_F32;
+    if (stages & kStageDkdv) {
+        hipError_t e = r.dtype == S2ATTN_F32 ? s2::launch_bwd_dkdv_f32(p, stream)
+                                              : s2::launch_bwd_dkdv_bf16(p, gf, stream);
+        if (e != hipSuccess) return S2ATTN_ERR_HIP;
+    }
+    if (stages & kStageDq) {
+        hipError_t e = r.dtype == S2ATTN_F32 ? s2::launch_bwd_dq_f32(p, stream)
+                                              : s2::launch_bwd_dq_bf16(p, gf, stream);
+        if (e != hipSuccess) return S2ATTN_ERR_HIP;
+    }
+    return S2ATTN_OK;
 }
 
 }  // namespace
@@ -234,7 +248,7 @@ int s2attn_bwd(const void* q, const void* k, const void* v, const void* o, const
                int Hq, int Hkv, int d, int G, int shifted_heads, hipStream_t stream) {
     if (!delta_ws) return S2ATTN_ERR_INVALID_ARG;
     return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, delta_ws, B, L, Hq, Hkv, d, G,
-                    shifted_heads, nullptr, nullptr, 0, stream);
+                    shifted_heads, nullptr, nullptr, 0, stream, kStageAll);
 }
 
 size_t s2attn_workspace_size(int is_bwd, int B, int L, int Hq, int Hkv, int d, int G,
@@ -257,7 +271,22 @@ int s2attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, co
                   int d, int G, int shifted_heads, const s2attn_opts* opts, void* ws,
                   size_t ws_bytes, hipStream_t stream) {
     return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, nullptr, B, L, Hq, Hkv, d, G,
-                    shifted_heads, opts, ws, ws_bytes, stream);
+                    shifted_heads, opts, ws, ws_bytes, stream, kStageAll);
+}
+
+int s2attn_bwd_stage_ex(int stage, const void* q, const void* k, const void* v, const void* o,
+                        const float* lse, const void* dout, void* dq, void* dk, void* dv, int B,
+                        int L, int Hq, int Hkv, int d, int G, int shifted_heads,
+                        const s2attn_opts* opts, void* ws, size_t ws_bytes, hipStream_t stream) {
+    int mask;
+    switch (stage) {
+        case S2ATTN_BWD_STAGE_PRE: mask = kStagePre; break;
+        case S2ATTN_BWD_STAGE_DKDV: mask = kStageDkdv; break;
+        case S2ATTN_BWD_STAGE_DQ: mask = kStageDq; break;
+        default: return S2ATTN_ERR_INVALID_ARG;
+    }
+    return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, nullptr, B, L, Hq, Hkv, d, G,
+                    shifted_heads, opts, ws, ws_bytes, stream, mask);
 }
 
 const char* s2attn_status_string(int status) {

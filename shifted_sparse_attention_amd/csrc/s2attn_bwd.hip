@@ -631,35 +631,52 @@ hipError_t launch_rope_prepass(const Params& p, void* q_out, void* k_out, hipStr
 }
 
 template <int D, bool GF>
-static hipError_t launch_bwd_bf16_t(const Params& p, hipStream_t st) {
+static void launch_dkdv_t(const Params& p, hipStream_t st) {
     const int n_kt = (p.G + DKV_BK - 1) / DKV_BK;
-    const long b1 = (long)p.B * p.Hkv * p.n_g * n_kt;
-    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, GF>), dim3(b1), dim3(256), 0, st, p, n_kt);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    const long blocks = (long)p.B * p.Hkv * p.n_g * n_kt;
+    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, GF>), dim3(blocks), dim3(256), 0, st, p, n_kt);
+}
+
+template <int D, bool GF>
+static void launch_dq_t(const Params& p, hipStream_t st) {
     const int n_qt = (p.G + DQ_BQ - 1) / DQ_BQ;
-    const long b2 = (long)p.B * p.Hq * p.n_g * n_qt;
-    hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, GF>), dim3(b2), dim3(256), 0, st, p, n_qt);
+    const long blocks = (long)p.B * p.Hq * p.n_g * n_qt;
+    hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, GF>), dim3(blocks), dim3(256), 0, st, p, n_qt);
+}
+
+hipError_t launch_bwd_dkdv_bf16(const Params& p, int grad_f32, hipStream_t st) {
+    if (p.d == 128)
+        grad_f32 ? launch_dkdv_t<128, true>(p, st) : launch_dkdv_t<128, false>(p, st);
+    else
+        grad_f32 ? launch_dkdv_t<64, true>(p, st) : launch_dkdv_t<64, false>(p, st);
     return hipGetLastError();
 }
 
-hipError_t launch_bwd_bf16(const Params& p, int grad_f32, hipStream_t st) {
+hipError_t launch_bwd_dq_bf16(const Params& p, int grad_f32, hipStream_t st) {
     if (p.d == 128)
-        return grad_f32 ? launch_bwd_bf16_t<128, true>(p, st) : launch_bwd_bf16_t<128, false>(p, st);
-    return grad_f32 ? launch_bwd_bf16_t<64, true>(p, st) : launch_bwd_bf16_t<64, false>(p, st);
+        grad_f32 ? launch_dq_t<128, true>(p, st) : launch_dq_t<128, false>(p, st);
+    else
+        grad_f32 ? launch_dq_t<64, true>(p, st) : launch_dq_t<64, false>(p, st);
+    return hipGetLastError();
 }
 
-hipError_t launch_bwd_f32(const Params& p, hipStream_t st) {
+hipError_t launch_bwd_dkdv_f32(const Params& p, hipStream_t st) {
     const int n_kt = (p.G + F32_ROWS - 1) / F32_ROWS;
-    const long b1 = (long)p.B * p.Hkv * p.n_g * n_kt;
-    const long b2 = (long)p.B * p.Hq * p.n_g * n_kt;
-    if (p.d == 128) {
-        hipLaunchKernelGGL(bwd_dkdv_f32_kernel<128>, dim3(b1), dim3(F32_ROWS), 0, st, p, n_kt);
-        hipLaunchKernelGGL(bwd_dq_f32_kernel<128>, dim3(b2), dim3(F32_ROWS), 0, st, p, n_kt);
-    } else {
-        hipLaunchKernelGGL(bwd_dkdv_f32_kernel<64>, dim3(b1), dim3(F32_ROWS), 0, st, p, n_kt);
-        hipLaunchKernelGGL(bwd_dq_f32_kernel<64>, dim3(b2), dim3(F32_ROWS), 0, st, p, n_kt);
-    }
+    const long blocks = (long)p.B * p.Hkv * p.n_g * n_kt;
+    if (p.d == 128)
+        hipLaunchKernelGGL(bwd_dkdv_f32_kernel<128>, dim3(blocks), dim3(F32_ROWS), 0, st, p, n_kt);
+    else
+        hipLaunchKernelGGL(bwd_dkdv_f32_kernel<64>, dim3(blocks), dim3(F32_ROWS), 0, st, p, n_kt);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq_f32(const Params& p, hipStream_t st) {
+    const int n_qt = (p.G + F32_ROWS - 1) / F32_ROWS;
+    const long blocks = (long)p.B * p.Hq * p.n_g * n_qt;
+    if (p.d == 128)
+        hipLaunchKernelGGL(bwd_dq_f32_kernel<128>, dim3(blocks), dim3(F32_ROWS), 0, st, p, n_qt);
+    else
+        hipLaunchKernelGGL(bwd_dq_f32_kernel<64>, dim3(blocks), dim3(F32_ROWS), 0, st, p, n_qt);
     return hipGetLastError();
 }
 

@@ -172,6 +172,17 @@ def test_python_wrappers_raise_named_errors():
 def test_header_documents_each_entry_point():
     src = open(HEADER).read()
     for name in declared_functions():
-        i = src.index(name + "(")
-        before = src[max(0, i - 600):i]
-        assert "/*" in before, f"{name} lacks a comment"
+        m = re.search(r"(\*/)\s*(?:const\s+)?[\w\s\*]*\b" + name + r"\s*\(", src)
+        assert m, f"{name} is not directly preceded by a comment"
+
+
+def test_bwd_stage_checks():
+    o = s2.s2attn_opts_init()
+    need = s2.s2attn_workspace_size(1, 1, 256, 4, 4, 64, 64, o)
+    for bad_stage in (-1, 3, 100):
+        st = L.lib().s2attn_bwd_stage_ex(bad_stage, *([FAKE] * 9), 1, 256, 4, 4, 64, 64, 2,
+                                         ctypes.byref(o), FAKE, need, None)
+        assert st == INV
+    st = L.lib().s2attn_bwd_stage_ex(L.S2ATTN_BWD_STAGE_DKDV, *([FAKE] * 9), 1, 256, 4, 4, 64, 64,
+                                     2, ctypes.byref(o), None, 0, None)
+    assert st == WS
