@@ -105,8 +105,8 @@ int s2attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 /*
  * Backward, bf16 inputs and gradients, scale 1/sqrt(d), no RoPE.
  * Reads q, k, v, o, lse (as written by s2attn_fwd on the same inputs) and
- * dout; writes dq, dk, dv.  delta_ws is caller scratch of B*Hq*L floats
- * (receives rowsum(dout * o)).  Gradient formulas: with P the attention
+ * dout; writes dq, dk, dv.  delta_ws is caller scratch of 2*B*Hq*L floats
+ * (receives rowsum(dout * o) and lse * log2(e), each [B, Hq, L]).  Gradient formulas: with P the attention
  * probabilities, dS = P * (dout . v_j - delta), dq = scale dS k,
  * dk = scale dS^T q, dv = P^T dout (summed over query heads per KV head).
  */

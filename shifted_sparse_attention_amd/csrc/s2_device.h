@@ -97,6 +97,48 @@ __device__ __forceinline__ bf16x8 to_bf16x8(const float* x) {
     return r;
 }
 
+// ---------------------------------------------------------------------------
+// Direct global -> LDS loads (gfx950 global_load_lds_dwordx4 / _dword): lane i
+// of the wave deposits its 16 (or 4) bytes at lds_base + 16 i (4 i), so one
+// instruction fills 1 KB of LDS with no registers in between.  The LDS base is
+// wave-uniform and travels in M0.
+//
+// They are issued from inline assembly on purpose: the compiler cannot tell
+// which of the two tile buffers a DMA targets, and when it sees one in flight
+// it waits for it before every transposed LDS read, serialising the prefetch
+// of the next tile with the work on the current one.  Here no waits are
+// inserted for them; completion is awaited explicitly (wait_vmem) before the
+// barrier that hands the buffer to the readers.  Nothing else in these
+// kernels uses M0.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t lds_addr(const char* lds) {
+    return __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)lds);
+}
+__device__ __forceinline__ void dma16(const void* gsrc, char* lds_base) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :: "s"(lds_addr(lds_base)), "v"(gsrc) : "memory");
+}
+__device__ __forceinline__ void dma4(const void* gsrc, char* lds_base) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+                 :: "s"(lds_addr(lds_base)), "v"(gsrc) : "memory");
+}
+__device__ __forceinline__ void wait_vmem() {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt/lgkmcnt untouched
+}
+
+// One 1 KB chunk `cc` of a row-major swizzled tile with D bf16 columns: the
+// tile row and the logical 16-byte column slot that lane `lane` must fetch so
+// that the DMA lands it at its swizzled place (the XOR swizzle is its own inverse).
+template <int D>
+__device__ __forceinline__ void dma_slot(int cc, int lane, int* row, int* col) {
+    constexpr int LPR = D / 8;  // lanes (16-byte slots) per row
+    const int r = cc * (64 / LPR) + lane / LPR;
+    const int phys = lane % LPR;
+    *row = r;
+    *col = 8 * (phys ^ swz(r));
+}
+
 // Work decode shared by the tiled kernels: unit (b, h, g) and tile index
 // from the flat block id.  Workgroups are dispatched round-robin over the 8
 // XCDs; when the unit count is a multiple of 8, every tile of a unit lands

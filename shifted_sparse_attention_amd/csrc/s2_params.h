@@ -18,17 +18,19 @@ struct Params {
     void* dq;
     void* dk;
     void* dv;
-    float* delta;
+    float* delta;   // [B, Hq, L] rowsum(dout * o), then [B, Hq, L] lse * log2(e)
+    float* lse2;
     // Sizes.
     int B, L, Hq, Hkv, d, G, shifted_heads;
     int r;          // Hq / Hkv
     int n_g;        // L / G
     float scale;    // softmax scale
     float scale_log2;  // scale * log2(e)
-    // RoPE with position interpolation: angle = t * rope_pos_scale * rope_base^(-2c/d).
+    // RoPE with position interpolation: angle = t * pos_scale * rope_base^(-2c/d), with
+    // pos_scale = L0 / L.  rope_rev[c] is that angle per unit of t, in revolutions
+    // (divided by 2 pi), formed in double precision on the host.
     int rope;
-    float rope_base;
-    double rope_pos_scale;
+    double rope_rev[64];
 };
 
 // Head shift: half a group for the last `shifted_heads` query heads.

@@ -69,7 +69,8 @@ int resolve_opts(const s2attn_opts* o, int d, Resolved* r) {
 
 size_t elem_size(int dtype) { return dtype == S2ATTN_F32 ? 4 : 2; }
 
-// Workspace layout: [delta (bwd) | rotated q | rotated k], each 256-byte aligned.
+// Workspace layout: [row terms (bwd): delta and lse*log2(e) | rotated q | rotated k],
+// each 256-byte aligned.
 struct WsLayout {
     size_t delta_off, delta_bytes;
     size_t rq_off, rq_bytes;
@@ -82,7 +83,7 @@ WsLayout ws_layout(int is_bwd, int B, int L, int Hq, int Hkv, int d, const Resol
     size_t off = 0;
     if (is_bwd) {
         w.delta_off = off;
-        w.delta_bytes = (size_t)B * Hq * L * sizeof(float);
+        w.delta_bytes = 2 * (size_t)B * Hq * L * sizeof(float);
         off += align_up(w.delta_bytes);
     }
     if (r.rope) {
@@ -113,8 +114,13 @@ s2::Params make_params(int B, int L, int Hq, int Hkv, int d, int G, int shifted_
     p.scale = r.scale;
     p.scale_log2 = r.scale * 1.4426950408889634f;
     p.rope = r.rope;
-    p.rope_base = r.rope_base;
-    p.rope_pos_scale = (double)r.rope_orig_len / (double)L;
+    if (r.rope) {
+        // LongLoRA blog, section 3.4: positions [0, L) are squeezed onto [0, L0).
+        const double pos_scale = (double)r.rope_orig_len / (double)L;
+        const double two_pi = 6.283185307179586476925286766559;
+        for (int c = 0; c < d / 2; ++c)
+            p.rope_rev[c] = pos_scale * pow((double)r.rope_base, -2.0 * c / (double)d) / two_pi;
+    }
     return p;
 }
 
@@ -194,6 +200,7 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const f
     p.dk = dk;
     p.dv = dv;
     p.delta = delta;
+    p.lse2 = delta + (size_t)B * Hq * L;
 
     char* rq = base + wl.rq_off;
     char* rk = base + wl.rk_off;

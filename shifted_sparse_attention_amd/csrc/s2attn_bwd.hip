@@ -14,7 +14,8 @@
 namespace s2 {
 
 // ---------------------------------------------------------------------------
-// delta[b, h, t] = sum_c dO[b, t, h, c] * O[b, t, h, c]   (fp32)
+// delta[b, h, t] = sum_c dO[b, t, h, c] * O[b, t, h, c]   (fp32), and the
+// LSE in base 2, lse2[b, h, t] = lse[b, h, t] * log2(e), for exp2 in the loops.
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(Params p, long n_rows) {
@@ -37,22 +38,25 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(Params p, long n_rows) {
         const long bt = row / p.Hq;
         const int t = (int)(bt % p.L);
         const int b = (int)(bt / p.L);
-        p.delta[lse_idx(p, b, h, t)] = acc;
+        const size_t li = lse_idx(p, b, h, t);
+        p.delta[li] = acc;
+        p.lse2[li] = p.lse[li] * kLog2e;
     }
 }
 
 // ---------------------------------------------------------------------------
-// RoPE with position interpolation.  Angle for original position t and
-// channel pair c: t * pos_scale * base^(-2c/d) (LongLoRA blog, section 3.4),
-// formed and reduced modulo 2*pi in double precision so that the float
-// sine/cosine see an argument below pi whatever the position.
+// RoPE with position interpolation (LongLoRA blog, section 3.4): channel pair
+// (c, c + d/2) of original position t turns by t * (L0/L) * base^(-2c/d).
+// The angle is formed in revolutions in double precision and reduced to
+// [-1/2, 1/2] there, so the hardware sine / cosine (which take revolutions)
+// see a small argument whatever the position.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void rope_cs(const Params& p, int t, int c, float* cs, float* sn) {
-    const double omega = pow((double)p.rope_base, -2.0 * (double)c / (double)p.d);
-    const double th = (double)t * p.rope_pos_scale * omega;
-    const double two_pi = 6.283185307179586476925286766559;
-    const double red = th - two_pi * rint(th / two_pi);
-    sincosf((float)red, sn, cs);
+    double r = (double)t * p.rope_rev[c];
+    r -= rint(r);
+    const float x = (float)r;
+    *sn = __builtin_amdgcn_sinf(x);
+    *cs = __builtin_amdgcn_cosf(x);
 }
 
 // Rotated copies of q and k (bf16 in, bf16 out), one thread per channel pair.
@@ -78,33 +82,172 @@ __global__ __launch_bounds__(256) void rope_prepass_kernel(Params p, bf16* qo, b
 }
 
 // ---------------------------------------------------------------------------
-// bf16 dK / dV.  A workgroup owns 128 keys (4 waves x 32) of one KV head and
-// group; K and V of a wave's keys stay in registers as MFMA B operands.  It
-// loops over the query heads sharing the KV head and over 64-query tiles at
-// or after its keys, staging Q and dO tiles (and their LSE and delta) in LDS.
-//   S  = Q K^T, dP = dO V^T           (M = query, N = key; A from LDS rows)
+// Gradient rows out of the accumulators.  A wave's accumulator holds row
+// row0 + l32 and channels 32cb + 8j + 4hh + e (the O^T layout of the MFMA).
+// `grad_rows` scales them (and rotates dq~ / dk~ back when RoPE was applied);
+// bf16 rows are then staged in LDS and written as whole rows by
+// `flush_rows`, fp32 rows go straight from registers.
+// ---------------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ void grad_rows(const Params& p, f32x16* acc, float mul, int g, int s,
+                                          int row0, int lane, bool rope_rows) {
+    constexpr int CB = D / 32;
+    const int hh = lane >> 5, l32 = lane & 31;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) acc[cb] *= mul;
+    if (rope_rows) {
+        const int i = row0 + l32;
+        const int t = orig_row(g, p.G, i < p.G ? i : 0, s, p.L);
+        // pairs (c, c + D/2) sit in blocks cb and cb + CB/2 of the same lane
+#pragma unroll
+        for (int cb = 0; cb < CB / 2; ++cb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int c = 32 * cb + 8 * (e >> 2) + 4 * hh + (e & 3);
+                float cs, sn;
+                rope_cs(p, t, c, &cs, &sn);
+                const float g1 = acc[cb][e], g2 = acc[cb + CB / 2][e];
+                acc[cb][e] = g1 * cs + g2 * sn;
+                acc[cb + CB / 2][e] = -g1 * sn + g2 * cs;
+            }
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void stage_rows_bf16(const f32x16* r_, char* stage_lds, int lane) {
+    constexpr int CB = D / 32;
+    const int hh = lane >> 5, l32 = lane & 31;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            bf16x4 a;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) a[e] = (bf16)r_[cb][4 * j + e];
+            *reinterpret_cast<bf16x4*>(stage_lds + tile_off<D>(l32, 32 * cb + 8 * j + 4 * hh)) = a;
+        }
+}
+
+template <int D>
+__device__ __forceinline__ void store_rows_f32(const Params& p, const f32x16* r_, void* dst, int b,
+                                               int H, int h, int g, int s, int row0, int lane) {
+    constexpr int CB = D / 32;
+    const int hh = lane >> 5, l32 = lane & 31;
+    const int i = row0 + l32;
+    if (i >= p.G) return;
+    const int t = orig_row(g, p.G, i, s, p.L);
+    float* out = static_cast<float*>(dst) + ((size_t)(b * (size_t)p.L + t) * H + h) * D;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            f32x4 a;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) a[e] = r_[cb][4 * j + e];
+            *reinterpret_cast<f32x4*>(out + 32 * cb + 8 * j + 4 * hh) = a;
+        }
+}
+
+// Write 32 staged bf16 rows as whole rows (LPR lanes per row, 16 bytes each).
+template <int D>
+__device__ __forceinline__ void flush_rows(const Params& p, const char* stage_lds, void* dst, int b,
+                                           int H, int h, int g, int s, int row0, int lane) {
+    constexpr int LPR = D / 8;
+    bf16* out = static_cast<bf16*>(dst);
+#pragma unroll
+    for (int it = 0; it < 32 * LPR / 64; ++it) {
+        const int id = it * 64 + lane;
+        const int row = id / LPR, col = (id % LPR) * 8;
+        const int i = row0 + row;
+        if (i < p.G) {
+            const u32x4 val = *reinterpret_cast<const u32x4*>(stage_lds + tile_off<D>(row, col));
+            const int t = orig_row(g, p.G, i, s, p.L);
+            *reinterpret_cast<u32x4*>(out + ((size_t)(b * (size_t)p.L + t) * H + h) * D + col) = val;
+        }
+    }
+}
+
+// Sum a key group's two partial accumulators (the wave with qh = 1 hands
+// its partial to the wave with qh = 0 through LDS) and store the rows.
+// Every wave of the workgroup calls it (it holds workgroup barriers).
+template <int D, bool GRAD_F32>
+__device__ __forceinline__ void reduce_store(const Params& p, f32x16 (&acc)[D / 32], f32x4* red,
+                                             char* stg, float mul, bool rope_rows, void* dst,
+                                             int b, int hk, int g, int s, int kw, int lane,
+                                             int qh) {
+    constexpr int CB = D / 32;
+    __syncthreads();  // previous readers of the LDS areas are done
+    if (qh == 1) {
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                red[(cb * 4 + j) * 64 + lane] = f32x4{acc[cb][4 * j], acc[cb][4 * j + 1],
+                                                      acc[cb][4 * j + 2], acc[cb][4 * j + 3]};
+    }
+    __syncthreads();
+    if (qh == 0) {
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const f32x4 o = red[(cb * 4 + j) * 64 + lane];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[cb][4 * j + e] += o[e];
+            }
+        grad_rows<D>(p, acc, mul, g, s, kw, lane, rope_rows);
+    }
+    if (GRAD_F32) {
+        if (qh == 0) store_rows_f32<D>(p, acc, dst, b, p.Hkv, hk, g, s, kw, lane);
+        return;
+    }
+    if (qh == 0) stage_rows_bf16<D>(acc, stg, lane);
+    __syncthreads();
+    if (qh == 0) flush_rows<D>(p, stg, dst, b, p.Hkv, hk, g, s, kw, lane);
+}
+
+// ---------------------------------------------------------------------------
+// bf16 dK / dV.  A workgroup owns 128 keys of one KV head and group, held by
+// 8 waves: waves w and w+4 share keys 32(w%4) .. +31 and split every 64-query
+// tile into its first and second 32 queries; each keeps partial dK, dV for
+// its keys, and the two halves are summed through LDS at the end.  The K and
+// V rows of the workgroup's keys sit in LDS for the whole kernel (MFMA B
+// operands).  The workgroup walks the query heads sharing the KV head and,
+// for each, the 64-query tiles at or after its keys; Q, dO, LSE and delta of
+// the next tile stream into the other of two LDS buffers while the current
+// one is consumed.
+//   S  = Q K^T, dP = dO V^T           (M = query, N = key; A and B from LDS rows)
 //   dV^T += dO^T P,  dK^T += Q^T dS   (M = channel, K = query; A from
 //                                      transposed LDS reads, B = P / dS
 //                                      straight from the score registers)
 // ---------------------------------------------------------------------------
+constexpr int DKV_WAVES = 8;
 constexpr int DKV_BK = 128;
 constexpr int DKV_BQ = 64;
 
 template <int D, bool GRAD_F32>
-__global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(Params p, int n_kt) {
+__global__ __launch_bounds__(64 * DKV_WAVES) void bwd_dkdv_bf16_kernel(Params p, int n_kt) {
     constexpr int KS = D / 16;
     constexpr int CB = D / 32;
-    __shared__ __attribute__((aligned(16))) char smem[2 * DKV_BQ * D * 2];
-    __shared__ __attribute__((aligned(16))) float s_lse[DKV_BQ];
-    __shared__ __attribute__((aligned(16))) float s_dl[DKV_BQ];
-    char* sQ = smem;
-    char* sO = smem + DKV_BQ * D * 2;  // dO tile
+    constexpr int TILE = DKV_BQ * D * 2;             // one Q or dO tile
+    constexpr int KTILE = DKV_BK * D * 2;            // the workgroup's K (or V) rows
+    constexpr int NCH = TILE / 1024;
+    constexpr int KNCH = KTILE / 1024;
+    constexpr int BUF = 2 * TILE + 2 * DKV_BQ * 4;   // Q, dO, lse2, delta
+    constexpr int RED = CB * 4 * 64 * 16;            // one wave's fp32 partial (dK or dV)
+    static_assert(4 * RED <= 2 * BUF + 2 * KTILE, "reduction area");
+    __shared__ __attribute__((aligned(1024))) char smem[2 * KTILE + 2 * BUF];
+    char* sKt = smem;
+    char* sVt = smem + KTILE;
+    char* bufs = smem + 2 * KTILE;
 
     const int n_units = p.B * p.Hkv * p.n_g;
     Work w = decode_work(blockIdx.x, n_units, n_kt, p.Hkv, p.n_g);
     w.tile = n_kt - 1 - w.tile;  // key tile 0 has the most queries: issue it first
     const int hk = w.h;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int kg = wave & 3, qh = wave >> 2;  // key group, query half
     const int hh = lane >> 5, l32 = lane & 31;
     const int g16 = lane >> 4, jj = lane & 15;
     const int s = head_shift(p, hk * p.r);  // all query heads of this KV head share it
@@ -114,22 +257,48 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(Params p, int n_kt) 
     const bf16* __restrict__ dout = static_cast<const bf16*>(p.dout);
 
     const int k0 = w.tile * DKV_BK;
-    const int kw = k0 + wave * 32;     // first key of this wave
+    const int kw = k0 + kg * 32;       // first key of this wave
     const int kj = kw + l32;           // this lane's key
-    const bool k_valid = kj < p.G;
-    const int k_t = orig_row(w.g, p.G, k_valid ? kj : 0, s, p.L);
+    const int qt_first = k0 / DKV_BQ;
+    const int nq = (p.G + DKV_BQ - 1) / DKV_BQ - qt_first;
+    const int n_it = p.r * nq;
 
-    bf16x8 kf[KS], vf[KS];
-    {
-        const size_t off = kv_row(p, w.b, k_t, hk) + 8 * hh;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            u32x4 kr = k_valid ? ld_global16(k + off + 16 * ks) : u32x4{0, 0, 0, 0};
-            u32x4 vr = k_valid ? ld_global16(v + off + 16 * ks) : u32x4{0, 0, 0, 0};
-            kf[ks] = __builtin_bit_cast(bf16x8, kr);
-            vf[ks] = __builtin_bit_cast(bf16x8, vr);
-        }
+    // The workgroup's K and V rows (rows past the group clamped; their
+    // gradients are never stored).
+    for (int c = wave; c < 2 * KNCH; c += DKV_WAVES) {
+        const bool isv = c >= KNCH;
+        const int cc = isv ? c - KNCH : c;
+        int row, col;
+        dma_slot<D>(cc, lane, &row, &col);
+        const int j = min(k0 + row, p.G - 1);
+        const size_t off = kv_row(p, w.b, orig_row(w.g, p.G, j, s, p.L), hk) + col;
+        dma16((isv ? v : k) + off, (isv ? sVt : sKt) + cc * 1024);
     }
+    // Q, dO, lse2, delta of step `it` (query head hk*r + it/nq, tile qt_first + it%nq).
+    // Rows past the group are clamped to its last row and masked in the loop.
+    auto stage = [&](int it, int buf) {
+        char* base = bufs + buf * BUF;
+        const int h = hk * p.r + it / nq;
+        const int q0 = (qt_first + it % nq) * DKV_BQ;
+        for (int c = wave; c < 2 * NCH + 2; c += DKV_WAVES) {
+            if (c < 2 * NCH) {
+                const bool isg = c >= NCH;
+                const int cc = isg ? c - NCH : c;
+                int row, col;
+                dma_slot<D>(cc, lane, &row, &col);
+                const int i = min(q0 + row, p.G - 1);
+                const size_t off = q_row(p, w.b, orig_row(w.g, p.G, i, s, p.L), h) + col;
+                dma16((isg ? dout : q) + off, base + (isg ? TILE : 0) + cc * 1024);
+            } else {
+                const int i = min(q0 + lane, p.G - 1);
+                const size_t li = lse_idx(p, w.b, h, orig_row(w.g, p.G, i, s, p.L));
+                dma4(c == 2 * NCH ? p.lse2 + li : p.delta + li,
+                     base + 2 * TILE + (c - 2 * NCH) * DKV_BQ * 4);
+            }
+        }
+    };
+    stage(0, 0);
+
     f32x16 dk[CB], dv[CB];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
@@ -137,173 +306,110 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(Params p, int n_kt) 
         dv[cb] = f32x16{};
     }
 
-    const int qt_first = k0 / DKV_BQ;
-    const int n_qt = (p.G + DKV_BQ - 1) / DKV_BQ;
-    for (int hr = 0; hr < p.r; ++hr) {
-        const int h = hk * p.r + hr;
-        for (int qt = qt_first; qt < n_qt; ++qt) {
-            const int q0 = qt * DKV_BQ;
-            __syncthreads();
-            {
-                constexpr int CPR = D / 8;
-#pragma unroll
-                for (int c = tid; c < DKV_BQ * CPR; c += 256) {
-                    const int row = c / CPR, col = (c % CPR) * 8;
-                    const int i = q0 + row;
-                    u32x4 qr = {0, 0, 0, 0}, gr = {0, 0, 0, 0};
-                    if (i < p.G) {
-                        const size_t off = q_row(p, w.b, orig_row(w.g, p.G, i, s, p.L), h) + col;
-                        qr = ld_global16(q + off);
-                        gr = ld_global16(dout + off);
-                    }
-                    st_lds16(sQ, tile_off<D>(row, col), qr);
-                    st_lds16(sO, tile_off<D>(row, col), gr);
-                }
-                if (tid < DKV_BQ) {
-                    const int i = q0 + tid;
-                    float l2 = INFINITY, dl = 0.f;  // rows past the group: P = 0
-                    if (i < p.G) {
-                        const size_t li = lse_idx(p, w.b, h, orig_row(w.g, p.G, i, s, p.L));
-                        l2 = p.lse[li] * kLog2e;
-                        dl = p.delta[li];
-                    }
-                    s_lse[tid] = l2;
-                    s_dl[tid] = dl;
-                }
-            }
-            __syncthreads();
-            if (q0 + DKV_BQ - 1 < kw) continue;  // every query of the tile is before every key
-            const bool diag = q0 < kw + 31;
+    for (int it = 0; it < n_it; ++it) {
+        wait_vmem();
+        __syncthreads();
+        if (it + 1 < n_it) stage(it + 1, (it + 1) & 1);
+        const int qb = (qt_first + it % nq) * DKV_BQ + 32 * qh;  // first query of this wave
+        if (qb + 31 < kw) continue;  // every query of the half-tile is before every key
+        const bool masked = (qb < kw + 31) || (qb + 32 > p.G);
+        const char* sQ = bufs + (it & 1) * BUF + 32 * qh * D * 2;
+        const char* sO = sQ + TILE;
+        const float* s_l2 = reinterpret_cast<const float*>(bufs + (it & 1) * BUF + 2 * TILE) + 32 * qh;
+        const float* s_dl = s_l2 + DKV_BQ;
 
-            f32x16 sacc[2], pacc[2];
+        f32x16 sacc = f32x16{}, pacc = f32x16{};
 #pragma unroll
-            for (int mq = 0; mq < 2; ++mq) {
-                sacc[mq] = f32x16{};
-                pacc[mq] = f32x16{};
+        for (int ks = 0; ks < KS; ++ks) {
+            const int off = tile_off<D>(l32, 16 * ks + 8 * hh);
+            const int koff = tile_off<D>(32 * kg + l32, 16 * ks + 8 * hh);
+            sacc = mfma32(ld_lds16(sQ, off), ld_lds16(sKt, koff), sacc);
+            pacc = mfma32(ld_lds16(sO, off), ld_lds16(sVt, koff), pacc);
+        }
+        // P and dS; element i is query qb + 8(i/4) + 4hh + i%4 and key kj.
+        auto softmax_grad = [&](bool mask) {
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    const int off = tile_off<D>(32 * mq + l32, 16 * ks + 8 * hh);
-                    sacc[mq] = mfma32(ld_lds16(sQ, off), kf[ks], sacc[mq]);
-                    pacc[mq] = mfma32(ld_lds16(sO, off), vf[ks], pacc[mq]);
-                }
-            }
-            // P and dS.  Row (query) index of element i: 32mq + 8(i/4) + 4hh + i%4.
+            for (int j = 0; j < 4; ++j) {
+                const int r0 = 8 * j + 4 * hh;
+                const f32x4 l4 = *reinterpret_cast<const f32x4*>(&s_l2[r0]);
+                const f32x4 d4 = *reinterpret_cast<const f32x4*>(&s_dl[r0]);
 #pragma unroll
-            for (int mq = 0; mq < 2; ++mq) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int qr0 = 32 * mq + 8 * j + 4 * hh;
-                    const f32x4 l4 = *reinterpret_cast<const f32x4*>(&s_lse[qr0]);
-                    const f32x4 d4 = *reinterpret_cast<const f32x4*>(&s_dl[qr0]);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int i = 4 * j + e;
-                        float pv = __builtin_amdgcn_exp2f(sacc[mq][i] * p.scale_log2 - l4[e]);
-                        if (diag && kj > q0 + qr0 + e) pv = 0.f;
-                        sacc[mq][i] = pv;
-                        pacc[mq][i] = pv * (pacc[mq][i] - d4[e]);
+                for (int e = 0; e < 4; ++e) {
+                    const int i = 4 * j + e;
+                    float pv = __builtin_amdgcn_exp2f(fmaf(sacc[i], p.scale_log2, -l4[e]));
+                    if (mask) {
+                        const int qq = qb + r0 + e;
+                        if (kj > qq || qq >= p.G) pv = 0.f;
                     }
+                    sacc[i] = pv;
+                    pacc[i] = pv * (pacc[i] - d4[e]);
                 }
             }
-            bf16x8 pb[4], db[4];
+        };
+        if (masked)
+            softmax_grad(true);
+        else
+            softmax_grad(false);
+        bf16x8 pb[2], db[2];
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                float t1[8], t2[8];
+        for (int kk = 0; kk < 2; ++kk) {
+            float t1[8], t2[8];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    t1[i] = sacc[kk >> 1][8 * (kk & 1) + i];
-                    t2[i] = pacc[kk >> 1][8 * (kk & 1) + i];
-                }
-                pb[kk] = to_bf16x8(t1);
-                db[kk] = to_bf16x8(t2);
+            for (int i = 0; i < 8; ++i) {
+                t1[i] = sacc[8 * kk + i];
+                t2[i] = pacc[8 * kk + i];
             }
+            pb[kk] = to_bf16x8(t1);
+            db[kk] = to_bf16x8(t2);
+        }
 #pragma unroll
-            for (int cb = 0; cb < CB; ++cb) {
-                const int col = 32 * cb + 16 * (g16 & 1) + 4 * (jj & 3);
+        for (int cb = 0; cb < CB; ++cb) {
+            const int col = 32 * cb + 16 * (g16 & 1) + 4 * (jj & 3);
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    const int row = 16 * kk + 4 * hh + (jj >> 2);
-                    const bf16x8 go = cat(ld_lds_tr(sO, tile_off<D>(row, col)),
-                                          ld_lds_tr(sO, tile_off<D>(row + 8, col)));
-                    dv[cb] = mfma32(go, pb[kk], dv[cb]);
-                    const bf16x8 qq = cat(ld_lds_tr(sQ, tile_off<D>(row, col)),
-                                          ld_lds_tr(sQ, tile_off<D>(row + 8, col)));
-                    dk[cb] = mfma32(qq, db[kk], dk[cb]);
-                }
+            for (int kk = 0; kk < 2; ++kk) {
+                const int row = 16 * kk + 4 * hh + (jj >> 2);
+                const bf16x8 go = cat(ld_lds_tr(sO, tile_off<D>(row, col)),
+                                      ld_lds_tr(sO, tile_off<D>(row + 8, col)));
+                dv[cb] = mfma32(go, pb[kk], dv[cb]);
+                const bf16x8 qq = cat(ld_lds_tr(sQ, tile_off<D>(row, col)),
+                                      ld_lds_tr(sQ, tile_off<D>(row + 8, col)));
+                dk[cb] = mfma32(qq, db[kk], dk[cb]);
             }
         }
     }
 
-    if (!k_valid) return;
-    // Lane holds key kj, channels 32cb + 8j + 4hh + 0..3.
-    float dkr[CB][16];
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) dkr[cb][i] = dk[cb][i] * p.scale;
-    if (p.rope) {
-        // dk = R^T dk~ on pairs (c, c + D/2): blocks cb and cb + CB/2 of the same lane.
-#pragma unroll
-        for (int cb = 0; cb < CB / 2; ++cb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int c = 32 * cb + 8 * (i >> 2) + 4 * hh + (i & 3);
-                float cs, sn;
-                rope_cs(p, k_t, c, &cs, &sn);
-                const float g1 = dkr[cb][i], g2 = dkr[cb + CB / 2][i];
-                dkr[cb][i] = g1 * cs + g2 * sn;
-                dkr[cb + CB / 2][i] = -g1 * sn + g2 * cs;
-            }
-    }
-    const size_t off = kv_row(p, w.b, k_t, hk);
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int c = 32 * cb + 8 * j + 4 * hh;
-            if (GRAD_F32) {
-                f32x4 a, b;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    a[e] = dkr[cb][4 * j + e];
-                    b[e] = dv[cb][4 * j + e];
-                }
-                *reinterpret_cast<f32x4*>(static_cast<float*>(p.dk) + off + c) = a;
-                *reinterpret_cast<f32x4*>(static_cast<float*>(p.dv) + off + c) = b;
-            } else {
-                bf16x4 a, b;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    a[e] = (bf16)dkr[cb][4 * j + e];
-                    b[e] = (bf16)dv[cb][4 * j + e];
-                }
-                *reinterpret_cast<bf16x4*>(static_cast<bf16*>(p.dk) + off + c) = a;
-                *reinterpret_cast<bf16x4*>(static_cast<bf16*>(p.dv) + off + c) = b;
-            }
-        }
+    // Sum the two query halves (waves 4..7 hand their partials to waves 0..3),
+    // dK first, then dV, and write each out.
+    f32x4* red = reinterpret_cast<f32x4*>(smem + kg * RED);
+    char* stg = smem + 4 * RED + kg * 32 * D * 2;  // bf16 staging of one tensor's rows
+    reduce_store<D, GRAD_F32>(p, dk, red, stg, p.scale, p.rope != 0, p.dk, w.b, hk, w.g, s, kw,
+                              lane, qh);
+    reduce_store<D, GRAD_F32>(p, dv, red, stg, 1.0f, false, p.dv, w.b, hk, w.g, s, kw, lane, qh);
 }
 
 // ---------------------------------------------------------------------------
-// bf16 dQ.  A workgroup owns 128 queries (4 waves x 32) of one head and
-// group; Q and dO of a wave's queries stay in registers.  It loops over the
-// 64-key tiles up to its last query.
+// bf16 dQ.  8 waves x 32 queries per workgroup; Q and dO of a wave's queries
+// stay in registers.  K and V tiles of 64 keys up to the last query stream
+// through two LDS buffers by direct global->LDS loads.
 //   S^T = K Q^T, dP^T = V dO^T   (M = key; A from LDS rows, B from registers)
 //   dQ^T += K^T dS^T             (A by transposed LDS reads of the K tile)
 // ---------------------------------------------------------------------------
-constexpr int DQ_BQ = 128;
+constexpr int DQ_WAVES = 8;
+constexpr int DQ_BQ = 32 * DQ_WAVES;
 constexpr int DQ_BK = 64;
 
 template <int D, bool GRAD_F32>
-__global__ __launch_bounds__(256) void bwd_dq_bf16_kernel(Params p, int n_qt) {
+__global__ __launch_bounds__(64 * DQ_WAVES) void bwd_dq_bf16_kernel(Params p, int n_qt) {
     constexpr int KS = D / 16;
     constexpr int CB = D / 32;
-    __shared__ __attribute__((aligned(16))) char smem[2 * DQ_BK * D * 2];
-    char* sK = smem;
-    char* sV = smem + DQ_BK * D * 2;
+    constexpr int TILE = DQ_BK * D * 2;
+    constexpr int NCH = TILE / 1024;
+    __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * TILE];
 
     const int n_units = p.B * p.Hq * p.n_g;
     const Work w = decode_work(blockIdx.x, n_units, n_qt, p.Hq, p.n_g);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hh = lane >> 5, l32 = lane & 31;
     const int g16 = lane >> 4, jj = lane & 15;
     const int s = head_shift(p, w.h);
@@ -318,6 +424,22 @@ __global__ __launch_bounds__(256) void bwd_dq_bf16_kernel(Params p, int n_qt) {
     const int qi = qw + l32;
     const bool q_valid = qi < p.G;
     const int q_t = orig_row(w.g, p.G, q_valid ? qi : 0, s, p.L);
+    const int q_end = min(q0 + DQ_BQ, p.G);
+    const int n_kt = (q_end + DQ_BK - 1) / DQ_BK;
+
+    auto stage = [&](int kt, int buf) {
+        char* base = smem + buf * 2 * TILE;
+        for (int c = wave; c < 2 * NCH; c += DQ_WAVES) {
+            const bool isv = c >= NCH;
+            const int cc = isv ? c - NCH : c;
+            int row, col;
+            dma_slot<D>(cc, lane, &row, &col);
+            const int j = min(kt * DQ_BK + row, p.G - 1);
+            const size_t off = kv_row(p, w.b, orig_row(w.g, p.G, j, s, p.L), hk) + col;
+            dma16((isv ? v : k) + off, base + (isv ? TILE : 0) + cc * 1024);
+        }
+    };
+    stage(0, 0);
 
     bf16x8 qf[KS], gf[KS];
     {
@@ -333,37 +455,22 @@ __global__ __launch_bounds__(256) void bwd_dq_bf16_kernel(Params p, int n_qt) {
     float lse2 = 0.f, dl = 0.f;
     if (q_valid) {
         const size_t li = lse_idx(p, w.b, w.h, q_t);
-        lse2 = p.lse[li] * kLog2e;
+        lse2 = p.lse2[li];
         dl = p.delta[li];
     }
     f32x16 dq[CB];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) dq[cb] = f32x16{};
 
-    const int q_end = min(q0 + DQ_BQ, p.G);
-    const int n_kt = (q_end + DQ_BK - 1) / DQ_BK;
     for (int kt = 0; kt < n_kt; ++kt) {
         const int k0 = kt * DQ_BK;
+        wait_vmem();
         __syncthreads();
-        {
-            constexpr int CPR = D / 8;
-#pragma unroll
-            for (int c = tid; c < DQ_BK * CPR; c += 256) {
-                const int row = c / CPR, col = (c % CPR) * 8;
-                const int j = k0 + row;
-                u32x4 kr = {0, 0, 0, 0}, vr = {0, 0, 0, 0};
-                if (j < p.G) {
-                    const size_t off = kv_row(p, w.b, orig_row(w.g, p.G, j, s, p.L), hk) + col;
-                    kr = ld_global16(k + off);
-                    vr = ld_global16(v + off);
-                }
-                st_lds16(sK, tile_off<D>(row, col), kr);
-                st_lds16(sV, tile_off<D>(row, col), vr);
-            }
-        }
-        __syncthreads();
+        if (kt + 1 < n_kt) stage(kt + 1, (kt + 1) & 1);
         if (k0 > qw + 31) continue;
         const bool diag = (k0 + DQ_BK - 1 > qw);
+        const char* sK = smem + (kt & 1) * 2 * TILE;
+        const char* sV = sK + TILE;
 
         f32x16 sacc[2], pacc[2];
 #pragma unroll
@@ -377,15 +484,23 @@ __global__ __launch_bounds__(256) void bwd_dq_bf16_kernel(Params p, int n_qt) {
                 pacc[mb] = mfma32(ld_lds16(sV, off), gf[ks], pacc[mb]);
             }
         }
+        auto softmax_grad = [&](bool mask) {
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+            for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int key = k0 + 32 * mb + 8 * (i >> 2) + 4 * hh + (i & 3);
-                float pv = __builtin_amdgcn_exp2f(sacc[mb][i] * p.scale_log2 - lse2);
-                if (diag && key > qi) pv = 0.f;
-                pacc[mb][i] = pv * (pacc[mb][i] - dl);
-            }
+                for (int i = 0; i < 16; ++i) {
+                    float pv = __builtin_amdgcn_exp2f(fmaf(sacc[mb][i], p.scale_log2, -lse2));
+                    if (mask) {
+                        const int key = k0 + 32 * mb + 8 * (i >> 2) + 4 * hh + (i & 3);
+                        if (key > qi) pv = 0.f;
+                    }
+                    pacc[mb][i] = pv * (pacc[mb][i] - dl);
+                }
+        };
+        if (diag)
+            softmax_grad(true);
+        else
+            softmax_grad(false);
         bf16x8 db[4];
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
@@ -407,44 +522,16 @@ __global__ __launch_bounds__(256) void bwd_dq_bf16_kernel(Params p, int n_qt) {
         }
     }
 
-    if (!q_valid) return;
-    // Lane holds query qi, channels 32cb + 8j + 4hh + 0..3 (O^T accumulator layout).
-    float r_[CB][16];
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) r_[cb][i] = dq[cb][i] * p.scale;
-    if (p.rope) {
-#pragma unroll
-        for (int cb = 0; cb < CB / 2; ++cb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int c = 32 * cb + 8 * (i >> 2) + 4 * hh + (i & 3);
-                float cs, sn;
-                rope_cs(p, q_t, c, &cs, &sn);
-                const float g1 = r_[cb][i], g2 = r_[cb + CB / 2][i];
-                r_[cb][i] = g1 * cs + g2 * sn;
-                r_[cb + CB / 2][i] = -g1 * sn + g2 * cs;
-            }
+    grad_rows<D>(p, dq, p.scale, w.g, s, qw, lane, p.rope != 0);
+    if (GRAD_F32) {
+        store_rows_f32<D>(p, dq, p.dq, w.b, p.Hq, w.h, w.g, s, qw, lane);
+        return;
     }
-    const size_t off = q_row(p, w.b, q_t, w.h);
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int c = 32 * cb + 8 * j + 4 * hh;
-            if (GRAD_F32) {
-                f32x4 a;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) a[e] = r_[cb][4 * j + e];
-                *reinterpret_cast<f32x4*>(static_cast<float*>(p.dq) + off + c) = a;
-            } else {
-                bf16x4 a;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) a[e] = (bf16)r_[cb][4 * j + e];
-                *reinterpret_cast<bf16x4*>(static_cast<bf16*>(p.dq) + off + c) = a;
-            }
-        }
+    __syncthreads();  // every wave is done with the K/V buffers
+    char* st = smem + wave * 32 * D * 2;
+    stage_rows_bf16<D>(dq, st, lane);
+    __syncthreads();
+    flush_rows<D>(p, st, p.dq, w.b, p.Hq, w.h, w.g, s, qw, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -634,14 +721,16 @@ template <int D, bool GF>
 static void launch_dkdv_t(const Params& p, hipStream_t st) {
     const int n_kt = (p.G + DKV_BK - 1) / DKV_BK;
     const long blocks = (long)p.B * p.Hkv * p.n_g * n_kt;
-    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, GF>), dim3(blocks), dim3(256), 0, st, p, n_kt);
+    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, GF>), dim3(blocks), dim3(64 * DKV_WAVES), 0, st, p,
+                       n_kt);
 }
 
 template <int D, bool GF>
 static void launch_dq_t(const Params& p, hipStream_t st) {
     const int n_qt = (p.G + DQ_BQ - 1) / DQ_BQ;
     const long blocks = (long)p.B * p.Hq * p.n_g * n_qt;
-    hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, GF>), dim3(blocks), dim3(256), 0, st, p, n_qt);
+    hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, GF>), dim3(blocks), dim3(64 * DQ_WAVES), 0, st, p,
+                       n_qt);
 }
 
 hipError_t launch_bwd_dkdv_bf16(const Params& p, int grad_f32, hipStream_t st) {

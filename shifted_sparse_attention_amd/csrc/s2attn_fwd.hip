@@ -13,29 +13,34 @@
 namespace s2 {
 
 // ---------------------------------------------------------------------------
-// bf16 forward.  4 waves x 32 queries; K and V tiles of 64 keys staged in LDS.
+// bf16 forward.  8 waves x 32 queries per workgroup; K and V tiles of 64 keys
+// are staged in LDS by direct global->LDS loads into two buffers, so the next
+// tile streams in while the current one is consumed (one barrier per tile).
 // Scores are formed transposed, S^T = K Q^T, so a lane owns one query column
 // and 16 of the 32 keys of each 32-key block (the other 16 sit in lane ^ 32):
 // the row max needs one permlane32 swap, the row sum none until the end.
 // P^T feeds O^T += V^T P^T directly from the score registers; V is read from
-// its row-major tile with transposed LDS reads.
+// its row-major tile with transposed LDS reads.  The epilogue stages O through
+// LDS so that every global store writes whole rows.
 // ---------------------------------------------------------------------------
-constexpr int FWD_BM = 128;
+constexpr int FWD_WAVES = 8;
+constexpr int FWD_BM = 32 * FWD_WAVES;
 constexpr int FWD_BN = 64;
-constexpr int FWD_THREADS = 256;
+constexpr int FWD_THREADS = 64 * FWD_WAVES;
 
 template <int D>
 __global__ __launch_bounds__(FWD_THREADS) void fwd_bf16_kernel(Params p, int n_qt) {
     constexpr int KS = D / 16;  // MFMA k-steps over the head dimension
     constexpr int CB = D / 32;  // 32-channel blocks of the output
-    __shared__ __attribute__((aligned(16))) char smem[2 * FWD_BN * D * 2];
-    char* sK = smem;
-    char* sV = smem + FWD_BN * D * 2;
+    constexpr int TILE = FWD_BN * D * 2;
+    constexpr int NCH = TILE / 1024;  // 1 KB DMA chunks per tile
+    __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * TILE];
 
     const int n_units = p.B * p.Hq * p.n_g;
     const Work w = decode_work(blockIdx.x, n_units, n_qt, p.Hq, p.n_g);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int hh = lane >> 5, l32 = lane & 31;
+    const int g16 = lane >> 4, jj = lane & 15;
     const int s = head_shift(p, w.h);
     const int hk = w.h / p.r;
     const bf16* __restrict__ q = static_cast<const bf16*>(p.q);
@@ -46,10 +51,28 @@ __global__ __launch_bounds__(FWD_THREADS) void fwd_bf16_kernel(Params p, int n_q
     const int qw = q0 + wave * 32;   // first query (in-group index) of this wave
     const int qi = qw + l32;         // this lane's query
     const bool q_valid = qi < p.G;
-    const int q_t = orig_row(w.g, p.G, q_valid ? qi : 0, s, p.L);
+    const int q_end = min(q0 + FWD_BM, p.G);
+    const int n_kt = (q_end + FWD_BN - 1) / FWD_BN;
+
+    // K, V tile kt -> buffer `buf`.  Rows past the group are clamped to its last
+    // row: those keys come after every query, so the causal mask removes them.
+    auto stage = [&](int kt, int buf) {
+        char* base = smem + buf * 2 * TILE;
+        for (int c = wave; c < 2 * NCH; c += FWD_WAVES) {
+            const bool isv = c >= NCH;
+            const int cc = isv ? c - NCH : c;
+            int row, col;
+            dma_slot<D>(cc, lane, &row, &col);
+            const int j = min(kt * FWD_BN + row, p.G - 1);
+            const size_t off = kv_row(p, w.b, orig_row(w.g, p.G, j, s, p.L), hk) + col;
+            dma16((isv ? v : k) + off, base + (isv ? TILE : 0) + cc * 1024);
+        }
+    };
+    stage(0, 0);
 
     bf16x8 qf[KS];
     {
+        const int q_t = orig_row(w.g, p.G, q_valid ? qi : 0, s, p.L);
         const bf16* qr = q + q_row(p, w.b, q_t, w.h) + 8 * hh;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
@@ -63,31 +86,14 @@ __global__ __launch_bounds__(FWD_THREADS) void fwd_bf16_kernel(Params p, int n_q
     for (int cb = 0; cb < CB; ++cb) oacc[cb] = f32x16{};
     float m = -INFINITY, lsum = 0.f;
 
-    const int q_end = min(q0 + FWD_BM, p.G);
-    const int n_kt = (q_end + FWD_BN - 1) / FWD_BN;
-    const int g16 = lane >> 4, jj = lane & 15;
-
     for (int kt = 0; kt < n_kt; ++kt) {
         const int k0 = kt * FWD_BN;
+        wait_vmem();
         __syncthreads();
-        {
-            constexpr int CPR = D / 8;  // 16-byte chunks per row
-#pragma unroll
-            for (int c = tid; c < FWD_BN * CPR; c += FWD_THREADS) {
-                const int row = c / CPR, col = (c % CPR) * 8;
-                const int j = k0 + row;
-                u32x4 kr = {0, 0, 0, 0}, vr = {0, 0, 0, 0};
-                if (j < p.G) {
-                    const size_t off = kv_row(p, w.b, orig_row(w.g, p.G, j, s, p.L), hk) + col;
-                    kr = ld_global16(k + off);
-                    vr = ld_global16(v + off);
-                }
-                st_lds16(sK, tile_off<D>(row, col), kr);
-                st_lds16(sV, tile_off<D>(row, col), vr);
-            }
-        }
-        __syncthreads();
+        if (kt + 1 < n_kt) stage(kt + 1, (kt + 1) & 1);
         if (k0 > qw + 31) continue;  // every key of the tile is after every query of the wave
+        const char* sK = smem + (kt & 1) * 2 * TILE;
+        const char* sV = sK + TILE;
 
         f32x16 sacc[2];
 #pragma unroll
@@ -152,21 +158,35 @@ __global__ __launch_bounds__(FWD_THREADS) void fwd_bf16_kernel(Params p, int n_q
         }
     }
 
+    // Epilogue: O / l through LDS (each wave its own 32 rows), then whole-row stores.
     const float l_tot = xhalf_sum(lsum);
-    if (q_valid) {
-        const float inv = 1.0f / l_tot;
-        bf16* orow = static_cast<bf16*>(p.o) + q_row(p, w.b, q_t, w.h);
+    const float inv = 1.0f / l_tot;
+    __syncthreads();  // every wave is done with the K/V buffers
+    char* so = smem + wave * 32 * D * 2;
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
+    for (int cb = 0; cb < CB; ++cb) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                bf16x4 val;
+        for (int j = 0; j < 4; ++j) {
+            bf16x4 val;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) val[e] = (bf16)(oacc[cb][4 * j + e] * inv);
-                *reinterpret_cast<bf16x4*>(orow + 32 * cb + 8 * j + 4 * hh) = val;
-            }
+            for (int e = 0; e < 4; ++e) val[e] = (bf16)(oacc[cb][4 * j + e] * inv);
+            *reinterpret_cast<bf16x4*>(so + tile_off<D>(l32, 32 * cb + 8 * j + 4 * hh)) = val;
         }
-        if (hh == 0) p.lse[lse_idx(p, w.b, w.h, q_t)] = (m + log2f(l_tot)) * kLn2;
+    }
+    if (q_valid && hh == 0)
+        p.lse[lse_idx(p, w.b, w.h, orig_row(w.g, p.G, qi, s, p.L))] = (m + log2f(l_tot)) * kLn2;
+    __syncthreads();
+    constexpr int LPR = D / 8;
+    bf16* o = static_cast<bf16*>(p.o);
+#pragma unroll
+    for (int it = 0; it < 32 * LPR / 64; ++it) {
+        const int id = it * 64 + lane;
+        const int row = id / LPR, col = (id % LPR) * 8;
+        const int i = qw + row;
+        if (i < p.G) {
+            const u32x4 val = *reinterpret_cast<const u32x4*>(so + tile_off<D>(row, col));
+            *reinterpret_cast<u32x4*>(o + q_row(p, w.b, orig_row(w.g, p.G, i, s, p.L), w.h) + col) = val;
+        }
     }
 }
 

@@ -146,7 +146,7 @@ def test_workspace_sizes_and_checks():
     o = s2.s2attn_opts_init()
     B, Ln, Hq, Hkv, d, G = 1, 256, 4, 2, 64, 64
     assert s2.s2attn_workspace_size(0, B, Ln, Hq, Hkv, d, G, o) == 0
-    delta = B * Hq * Ln * 4
+    delta = 2 * B * Hq * Ln * 4     # delta and lse * log2(e)
     assert s2.s2attn_workspace_size(1, B, Ln, Hq, Hkv, d, G, o) == (delta + 255) // 256 * 256
     o.rope = 1
     rq, rk = B * Ln * Hq * d * 2, B * Ln * Hkv * d * 2

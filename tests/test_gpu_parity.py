@@ -325,7 +325,7 @@ def test_every_output_written_and_no_stray_writes():
     dqb, dq = padded(nq, BF)
     dkb, dk = padded(nk, BF)
     dvb, dv = padded(nk, BF)
-    deb, de = padded(nl, torch.float32)
+    deb, de = padded(2 * nl, torch.float32)   # delta and lse * log2(e)
     s2.s2attn_bwd(tq, tk, tv, o, lse, tdo, dq, dk, dv, de, B, L, Hq, Hkv, d, G, sh)
     torch.cuda.synchronize()
     for buf, body in ((ob, o), (lb, lse), (dqb, dq), (dkb, dk), (dvb, dv), (deb, de)):
