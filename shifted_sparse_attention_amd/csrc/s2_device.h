@@ -32,19 +32,24 @@ __device__ __forceinline__ int orig_row(int g, int G, int i, int s, int L) {
 }
 
 // ---------------------------------------------------------------------------
-// Row-major bf16 tiles of 128 (or 64) columns in LDS, 16-byte slots swizzled
-// by an XOR of the row so that both access patterns the kernels use spread
-// over the banks: 32 rows read at one 16-byte column slot (MFMA operand from
-// a row-major tile) and 4 rows x 32 bytes per 16 lanes (transposed reads).
+// Row-major bf16 tiles of D = 128 (or 64) columns in LDS, with the 16-byte
+// column slots of each row permuted by an XOR of the row.  The LDS serves 64
+// four-byte banks per cycle, i.e. 16 slots; the permutation makes both access
+// patterns of the kernels hit 16 distinct slots: 16 consecutive rows read at
+// one logical slot (MFMA operands from a row-major tile), and 4 consecutive
+// rows x 4 slots (transposed reads).  With 8 slots per row (D = 64) it covers
+// 8 rows / 4 rows x 2 slots.
 // ---------------------------------------------------------------------------
+template <int D>
 __device__ __forceinline__ int swz(int row) {
+    if constexpr (D == 128) return ((row & 3) << 2) ^ ((row >> 2) & 3);
     return ((row & 3) << 1) | ((row >> 2) & 1);
 }
 
 // Byte offset of element (row, col) in a row-major tile with `D` bf16 columns.
 template <int D>
 __device__ __forceinline__ int tile_off(int row, int col) {
-    int slot = (col >> 3) ^ swz(row);
+    int slot = (col >> 3) ^ swz<D>(row);
     return row * (D * 2) + slot * 16 + (col & 7) * 2;
 }
 
@@ -115,28 +120,41 @@ __device__ __forceinline__ uint32_t lds_addr(const char* lds) {
     return __builtin_amdgcn_readfirstlane(
         (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)lds);
 }
-__device__ __forceinline__ void dma16(const void* gsrc, char* lds_base) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-                 :: "s"(lds_addr(lds_base)), "v"(gsrc) : "memory");
+// gsrc = sbase + voff (voff a 32-bit byte offset, sbase wave-uniform).
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, char* lds_base) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :: "s"(lds_addr(lds_base)), "v"(voff), "s"(sbase) : "memory");
 }
-__device__ __forceinline__ void dma4(const void* gsrc, char* lds_base) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
-                 :: "s"(lds_addr(lds_base)), "v"(gsrc) : "memory");
+__device__ __forceinline__ void dma4(const void* sbase, uint32_t voff, char* lds_base) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+                 :: "s"(lds_addr(lds_base)), "v"(voff), "s"(sbase) : "memory");
 }
 __device__ __forceinline__ void wait_vmem() {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt/lgkmcnt untouched
 }
 
 // One 1 KB chunk `cc` of a row-major swizzled tile with D bf16 columns: the
-// tile row and the logical 16-byte column slot that lane `lane` must fetch so
-// that the DMA lands it at its swizzled place (the XOR swizzle is its own inverse).
+// tile row and the byte offset of the logical 16-byte column slot that lane
+// `lane` must fetch so that the DMA lands it at its swizzled place (the XOR
+// swizzle is its own inverse).
+struct ChunkSlot {
+    int row;
+    uint32_t colb;
+};
 template <int D>
-__device__ __forceinline__ void dma_slot(int cc, int lane, int* row, int* col) {
+__device__ __forceinline__ ChunkSlot chunk_slot(int cc, int lane) {
     constexpr int LPR = D / 8;  // lanes (16-byte slots) per row
     const int r = cc * (64 / LPR) + lane / LPR;
     const int phys = lane % LPR;
-    *row = r;
-    *col = 8 * (phys ^ swz(r));
+    return ChunkSlot{r, (uint32_t)(16 * (phys ^ swz<D>(r)))};
+}
+
+// Byte offset, within one (batch, head) plane of a [B, L, H, D] tensor, of
+// the row holding in-group index jg (clamped to the group's last row) of
+// group g under shift s.  rowbytes = H * D * 2 < 2^24.
+__device__ __forceinline__ uint32_t row_off(int g, int G, int jg, int s, int L, uint32_t rowbytes) {
+    const int t = orig_row(g, G, min(jg, G - 1), s, L);
+    return __umul24((uint32_t)t, rowbytes);
 }
 
 // Work decode shared by the tiled kernels: unit (b, h, g) and tile index

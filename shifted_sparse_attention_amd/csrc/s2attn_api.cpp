@@ -41,6 +41,9 @@ int check_sizes(int B, int L, int Hq, int Hkv, int d, int G, int shifted_heads) 
     const double wgs = (double)B * Hq * (L / G) * ((G + 63) / 64);
     if (wgs > 2147483647.0) return S2ATTN_ERR_UNSUPPORTED;
     if ((double)L * Hq > 2147483647.0) return S2ATTN_ERR_UNSUPPORTED;
+    // Tiles are fetched as a 64-bit (batch, head) base plus 32-bit byte offsets.
+    const int Hmax = Hq > Hkv ? Hq : Hkv;
+    if ((double)L * Hmax * d * 4 > 4294967295.0 || L >= (1 << 24)) return S2ATTN_ERR_UNSUPPORTED;
     return S2ATTN_OK;
 }
 

@@ -265,36 +265,40 @@ __global__ __launch_bounds__(64 * DKV_WAVES) void bwd_dkdv_bf16_kernel(Params p,
 
     // The workgroup's K and V rows (rows past the group clamped; their
     // gradients are never stored).
-    for (int c = wave; c < 2 * KNCH; c += DKV_WAVES) {
-        const bool isv = c >= KNCH;
-        const int cc = isv ? c - KNCH : c;
-        int row, col;
-        dma_slot<D>(cc, lane, &row, &col);
-        const int j = min(k0 + row, p.G - 1);
-        const size_t off = kv_row(p, w.b, orig_row(w.g, p.G, j, s, p.L), hk) + col;
-        dma16((isv ? v : k) + off, (isv ? sVt : sKt) + cc * 1024);
+    {
+        const uint32_t rowb = (uint32_t)p.Hkv * D * 2;
+        const size_t plane = ((size_t)w.b * p.L * p.Hkv + hk) * D;
+        for (int c = wave; c < 2 * KNCH; c += DKV_WAVES) {
+            const bool isv = c >= KNCH;
+            const int cc = isv ? c - KNCH : c;
+            const ChunkSlot sl = chunk_slot<D>(cc, lane);
+            const uint32_t off = row_off(w.g, p.G, k0 + sl.row, s, p.L, rowb) + sl.colb;
+            dma16((isv ? v : k) + plane, off, (isv ? sVt : sKt) + cc * 1024);
+        }
     }
     // Q, dO, lse2, delta of step `it` (query head hk*r + it/nq, tile qt_first + it%nq).
     // Rows past the group are clamped to its last row and masked in the loop.
+    constexpr int NSLOT = 2 * NCH / DKV_WAVES;  // 1 KB chunks per wave per tile; Q first, then dO
+    const uint32_t qrowb = (uint32_t)p.Hq * D * 2;
+    ChunkSlot slot[NSLOT];
+#pragma unroll
+    for (int j = 0; j < NSLOT; ++j) slot[j] = chunk_slot<D>((wave + DKV_WAVES * j) % NCH, lane);
     auto stage = [&](int it, int buf) {
         char* base = bufs + buf * BUF;
         const int h = hk * p.r + it / nq;
         const int q0 = (qt_first + it % nq) * DKV_BQ;
-        for (int c = wave; c < 2 * NCH + 2; c += DKV_WAVES) {
-            if (c < 2 * NCH) {
-                const bool isg = c >= NCH;
-                const int cc = isg ? c - NCH : c;
-                int row, col;
-                dma_slot<D>(cc, lane, &row, &col);
-                const int i = min(q0 + row, p.G - 1);
-                const size_t off = q_row(p, w.b, orig_row(w.g, p.G, i, s, p.L), h) + col;
-                dma16((isg ? dout : q) + off, base + (isg ? TILE : 0) + cc * 1024);
-            } else {
-                const int i = min(q0 + lane, p.G - 1);
-                const size_t li = lse_idx(p, w.b, h, orig_row(w.g, p.G, i, s, p.L));
-                dma4(c == 2 * NCH ? p.lse2 + li : p.delta + li,
-                     base + 2 * TILE + (c - 2 * NCH) * DKV_BQ * 4);
-            }
+        const size_t plane = ((size_t)w.b * p.L * p.Hq + h) * D;
+#pragma unroll
+        for (int j = 0; j < NSLOT; ++j) {
+            const bool isg = j >= NSLOT / 2;
+            const int cc = (wave + DKV_WAVES * j) % NCH;
+            const uint32_t off = row_off(w.g, p.G, q0 + slot[j].row, s, p.L, qrowb) + slot[j].colb;
+            dma16((isg ? dout : q) + plane, off, base + (isg ? TILE : 0) + cc * 1024);
+        }
+        if (wave < 2) {  // LSE (base 2) and delta of the tile's 64 queries
+            const float* rb = (wave == 0 ? p.lse2 : p.delta) + ((size_t)w.b * p.Hq + h) * p.L;
+            const uint32_t off = 4u * (uint32_t)orig_row(w.g, p.G, min(q0 + lane, p.G - 1), s, p.L);
+            dma4(rb, off, base + 2 * TILE + wave * DKV_BQ * 4);
         }
     };
     stage(0, 0);
@@ -427,16 +431,20 @@ __global__ __launch_bounds__(64 * DQ_WAVES) void bwd_dq_bf16_kernel(Params p, in
     const int q_end = min(q0 + DQ_BQ, p.G);
     const int n_kt = (q_end + DQ_BK - 1) / DQ_BK;
 
+    constexpr int NSLOT = 2 * NCH / DQ_WAVES;  // 1 KB chunks per wave per tile; K first, then V
+    const uint32_t rowb = (uint32_t)p.Hkv * D * 2;
+    const size_t plane = ((size_t)w.b * p.L * p.Hkv + hk) * D;
+    ChunkSlot slot[NSLOT];
+#pragma unroll
+    for (int j = 0; j < NSLOT; ++j) slot[j] = chunk_slot<D>((wave + DQ_WAVES * j) % NCH, lane);
     auto stage = [&](int kt, int buf) {
         char* base = smem + buf * 2 * TILE;
-        for (int c = wave; c < 2 * NCH; c += DQ_WAVES) {
-            const bool isv = c >= NCH;
-            const int cc = isv ? c - NCH : c;
-            int row, col;
-            dma_slot<D>(cc, lane, &row, &col);
-            const int j = min(kt * DQ_BK + row, p.G - 1);
-            const size_t off = kv_row(p, w.b, orig_row(w.g, p.G, j, s, p.L), hk) + col;
-            dma16((isv ? v : k) + off, base + (isv ? TILE : 0) + cc * 1024);
+#pragma unroll
+        for (int j = 0; j < NSLOT; ++j) {
+            const bool isv = j >= NSLOT / 2;
+            const int cc = (wave + DQ_WAVES * j) % NCH;
+            const uint32_t off = row_off(w.g, p.G, kt * DQ_BK + slot[j].row, s, p.L, rowb) + slot[j].colb;
+            dma16((isv ? v : k) + plane, off, base + (isv ? TILE : 0) + cc * 1024);
         }
     };
     stage(0, 0);

@@ -38,7 +38,8 @@ __global__ __launch_bounds__(FWD_THREADS) void fwd_bf16_kernel(Params p, int n_q
 
     const int n_units = p.B * p.Hq * p.n_g;
     const Work w = decode_work(blockIdx.x, n_units, n_qt, p.Hq, p.n_g);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hh = lane >> 5, l32 = lane & 31;
     const int g16 = lane >> 4, jj = lane & 15;
     const int s = head_shift(p, w.h);
@@ -56,16 +57,20 @@ __global__ __launch_bounds__(FWD_THREADS) void fwd_bf16_kernel(Params p, int n_q
 
     // K, V tile kt -> buffer `buf`.  Rows past the group are clamped to its last
     // row: those keys come after every query, so the causal mask removes them.
+    constexpr int NSLOT = 2 * NCH / FWD_WAVES;  // 1 KB chunks per wave per tile; K first, then V
+    const uint32_t rowb = (uint32_t)p.Hkv * D * 2;
+    const size_t plane = ((size_t)w.b * p.L * p.Hkv + hk) * D;
+    ChunkSlot slot[NSLOT];
+#pragma unroll
+    for (int j = 0; j < NSLOT; ++j) slot[j] = chunk_slot<D>((wave + FWD_WAVES * j) % NCH, lane);
     auto stage = [&](int kt, int buf) {
         char* base = smem + buf * 2 * TILE;
-        for (int c = wave; c < 2 * NCH; c += FWD_WAVES) {
-            const bool isv = c >= NCH;
-            const int cc = isv ? c - NCH : c;
-            int row, col;
-            dma_slot<D>(cc, lane, &row, &col);
-            const int j = min(kt * FWD_BN + row, p.G - 1);
-            const size_t off = kv_row(p, w.b, orig_row(w.g, p.G, j, s, p.L), hk) + col;
-            dma16((isv ? v : k) + off, base + (isv ? TILE : 0) + cc * 1024);
+#pragma unroll
+        for (int j = 0; j < NSLOT; ++j) {
+            const bool isv = j >= NSLOT / 2;
+            const int cc = (wave + FWD_WAVES * j) % NCH;
+            const uint32_t off = row_off(w.g, p.G, kt * FWD_BN + slot[j].row, s, p.L, rowb) + slot[j].colb;
+            dma16((isv ? v : k) + plane, off, base + (isv ? TILE : 0) + cc * 1024);
         }
     };
     stage(0, 0);
@@ -85,6 +90,8 @@ __global__ __launch_bounds__(FWD_THREADS) void fwd_bf16_kernel(Params p, int n_q
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) oacc[cb] = f32x16{};
     float m = -INFINITY, lsum = 0.f;
+    constexpr float kLazy = 8.0f;
+    const float lazy_raw = kLazy / p.scale_log2;
 
     for (int kt = 0; kt < n_kt; ++kt) {
         const int k0 = kt * FWD_BN;
@@ -106,36 +113,43 @@ __global__ __launch_bounds__(FWD_THREADS) void fwd_bf16_kernel(Params p, int n_q
             }
         }
 
-        const bool diag = (k0 + FWD_BN - 1 > qw);
+        // Raw scores; keys after the query are -inf (only on diagonal tiles).
+        if (k0 + FWD_BN - 1 > qw) {
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int key = k0 + 32 * mb + 8 * (i >> 2) + 4 * hh + (i & 3);
+                    if (key > qi) sacc[mb][i] = -INFINITY;
+                }
+        }
         float mx = -INFINITY;
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
+        for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int key = k0 + 32 * mb + 8 * (i >> 2) + 4 * hh + (i & 3);
-                float x = sacc[mb][i] * p.scale_log2;
-                if (diag && key > qi) x = -INFINITY;
-                sacc[mb][i] = x;
-                mx = fmaxf(mx, x);
-            }
-        }
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[mb][i]);
         mx = xhalf_max(mx);
-        const float m_new = fmaxf(m, mx);
-        const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-        m = m_new;
-        float ps = 0.f;
+        // The reference maximum m (raw score units) moves only when a score
+        // exceeds it by more than kLazy / scale_log2 (a factor 2^kLazy in the
+        // exponentials): O and l are then rescaled together, so every row
+        // keeps one consistent reference and the result is exact.
+        if (__builtin_amdgcn_ballot_w64(mx > m + lazy_raw) != 0) {
+            const float m_new = fmaxf(m, mx);
+            const float alpha = __builtin_amdgcn_exp2f((m - m_new) * p.scale_log2);
+            m = m_new;
+            lsum *= alpha;
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
+            for (int cb = 0; cb < CB; ++cb) oacc[cb] *= alpha;
+        }
+        const float mc = m * p.scale_log2;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const float e = __builtin_amdgcn_exp2f(sacc[mb][i] - m_new);
+                const float e = __builtin_amdgcn_exp2f(fmaf(sacc[mb][i], p.scale_log2, -mc));
                 sacc[mb][i] = e;
-                ps += e;
+                lsum += e;
             }
-        }
-        lsum = lsum * alpha + ps;
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb) oacc[cb] *= alpha;
 
         bf16x8 pb[4];
 #pragma unroll
@@ -174,7 +188,7 @@ __global__ __launch_bounds__(FWD_THREADS) void fwd_bf16_kernel(Params p, int n_q
         }
     }
     if (q_valid && hh == 0)
-        p.lse[lse_idx(p, w.b, w.h, orig_row(w.g, p.G, qi, s, p.L))] = (m + log2f(l_tot)) * kLn2;
+        p.lse[lse_idx(p, w.b, w.h, orig_row(w.g, p.G, qi, s, p.L))] = m * p.scale + log2f(l_tot) * kLn2;
     __syncthreads();
     constexpr int LPR = D / 8;
     bf16* o = static_cast<bf16*>(p.o);

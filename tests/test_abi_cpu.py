@@ -100,6 +100,7 @@ INV, UNS, WS = L.S2ATTN_ERR_INVALID_ARG, L.S2ATTN_ERR_UNSUPPORTED, L.S2ATTN_ERR_
     (dict(sh=-1), INV), (dict(sh=5), INV),                 # shifted_heads outside [0, Hq]
     (dict(L=255, G=51, sh=1), INV),                        # odd G with shifted heads
     (dict(d=96), UNS), (dict(d=32), UNS),
+    (dict(L=1 << 22, G=1 << 22, sh=0), UNS),   # one (batch, head) plane past 32-bit offsets
 ])
 def test_fwd_argument_checks(kw, want):
     assert fwd(**kw) == want
