@@ -112,6 +112,14 @@ __global__ __launch_bounds__(FWD_THREADS) void fwd_bf16_kernel(Params p, int n_q
                 sacc[mb] = mfma32(a, qf[ks], sacc[mb]);
             }
         }
+        // Keep several K reads in flight ahead of the MFMAs that consume them.
+        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+        for (int i = 0; i < 2 * KS - 6; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
 
         // Raw scores; keys after the query are -inf (only on diagonal tiles).
         if (k0 + FWD_BN - 1 > qw) {
@@ -170,6 +178,14 @@ __global__ __launch_bounds__(FWD_THREADS) void fwd_bf16_kernel(Params p, int n_q
                 oacc[cb] = mfma32(cat(a0, a1), pb[kk], oacc[cb]);
             }
         }
+        // Same for the transposed V reads (two per MFMA).
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+        for (int i = 0; i < 4 * CB - 4; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     }
 
     // Epilogue: O / l through LDS (each wave its own 32 rows), then whole-row stores.
