@@ -25,7 +25,7 @@ namespace s2 {
 // ---------------------------------------------------------------------------
 constexpr int FWD_WAVES = 8;
 constexpr int FWD_BM = 32 * FWD_WAVES;
-constexpr int FWD_BN = 64;
+constexpr int FWD_BN = 128;
 constexpr int FWD_THREADS = 64 * FWD_WAVES;
 
 template <int D>
@@ -34,6 +34,8 @@ __global__ __launch_bounds__(FWD_THREADS) void fwd_bf16_kernel(Params p, int n_q
     constexpr int CB = D / 32;  // 32-channel blocks of the output
     constexpr int TILE = FWD_BN * D * 2;
     constexpr int NCH = TILE / 1024;  // 1 KB DMA chunks per tile
+    constexpr int MB = FWD_BN / 32;   // 32-key blocks of a tile
+    constexpr int KK = FWD_BN / 16;   // 16-key MFMA k-steps of P V
     __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * TILE];
 
     const int n_units = p.B * p.Hq * p.n_g;
@@ -102,9 +104,9 @@ __global__ __launch_bounds__(FWD_THREADS) void fwd_bf16_kernel(Params p, int n_q
         const char* sK = smem + (kt & 1) * 2 * TILE;
         const char* sV = sK + TILE;
 
-        f32x16 sacc[2];
+        f32x16 sacc[MB];
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
+        for (int mb = 0; mb < MB; ++mb) {
             sacc[mb] = f32x16{};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
@@ -115,7 +117,7 @@ __global__ __launch_bounds__(FWD_THREADS) void fwd_bf16_kernel(Params p, int n_q
         // Keep several K reads in flight ahead of the MFMAs that consume them.
         __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
 #pragma unroll
-        for (int i = 0; i < 2 * KS - 6; ++i) {
+        for (int i = 0; i < MB * KS - 6; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
@@ -124,7 +126,7 @@ __global__ __launch_bounds__(FWD_THREADS) void fwd_bf16_kernel(Params p, int n_q
         // Raw scores; keys after the query are -inf (only on diagonal tiles).
         if (k0 + FWD_BN - 1 > qw) {
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
+            for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int key = k0 + 32 * mb + 8 * (i >> 2) + 4 * hh + (i & 3);
@@ -133,7 +135,7 @@ __global__ __launch_bounds__(FWD_THREADS) void fwd_bf16_kernel(Params p, int n_q
         }
         float mx = -INFINITY;
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+        for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[mb][i]);
         mx = xhalf_max(mx);
@@ -151,7 +153,7 @@ __global__ __launch_bounds__(FWD_THREADS) void fwd_bf16_kernel(Params p, int n_q
         }
         const float mc = m * p.scale_log2;
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+        for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const float e = __builtin_amdgcn_exp2f(fmaf(sacc[mb][i], p.scale_log2, -mc));
@@ -159,9 +161,9 @@ __global__ __launch_bounds__(FWD_THREADS) void fwd_bf16_kernel(Params p, int n_q
                 lsum += e;
             }
 
-        bf16x8 pb[4];
+        bf16x8 pb[KK];
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
+        for (int kk = 0; kk < KK; ++kk) {
             float tmp[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) tmp[i] = sacc[kk >> 1][8 * (kk & 1) + i];
@@ -171,7 +173,7 @@ __global__ __launch_bounds__(FWD_THREADS) void fwd_bf16_kernel(Params p, int n_q
         for (int cb = 0; cb < CB; ++cb) {
             const int col = 32 * cb + 16 * (g16 & 1) + 4 * (jj & 3);
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
+            for (int kk = 0; kk < KK; ++kk) {
                 const int row = 16 * kk + 4 * hh + (jj >> 2);
                 bf16x4 a0 = ld_lds_tr(sV, tile_off<D>(row, col));
                 bf16x4 a1 = ld_lds_tr(sV, tile_off<D>(row + 8, col));
@@ -181,7 +183,7 @@ __global__ __launch_bounds__(FWD_THREADS) void fwd_bf16_kernel(Params p, int n_q
         // Same for the transposed V reads (two per MFMA).
         __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
-        for (int i = 0; i < 4 * CB - 4; ++i) {
+        for (int i = 0; i < KK * CB - 4; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         }
