@@ -42,6 +42,54 @@ def kernel_source_sha():
     return h.hexdigest()[:16]
 
 
+class ClockSampler:
+    """Samples the shader clock the driver reports (pp_dpm_sclk, the level
+    marked '*') every few milliseconds while the timed region runs."""
+
+    def __init__(self, period_s=0.004):
+        import glob
+        import threading
+        paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.path = paths[0] if paths else None
+        self.period = period_s
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _read(self):
+        for line in open(self.path).read().splitlines():
+            if line.rstrip().endswith("*"):
+                return float(line.split(":")[1].strip().split("M")[0].split("m")[0])
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                v = self._read()
+            except (OSError, ValueError, IndexError):
+                v = None
+            if v is not None:
+                self.samples.append(v)
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        if self.path:
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self.path:
+            self._thread.join()
+
+    def summary(self):
+        if not self.samples:
+            return None
+        xs = self.samples
+        return {"mean": round(sum(xs) / len(xs), 1), "min": min(xs), "max": max(xs), "samples": len(xs),
+                "source": self.path}
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -118,11 +166,12 @@ def main():
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    start.record(stream)
-    for i in range(args.steps):
-        step(evs[i])
-    end.record(stream)
-    torch.cuda.synchronize()
+    with ClockSampler() as clk:
+        start.record(stream)
+        for i in range(args.steps):
+            step(evs[i])
+        end.record(stream)
+        torch.cuda.synchronize()
     ms_step = start.elapsed_time(end) / args.steps
     names = ["fwd", "bwd_pre", "bwd_dkdv", "bwd_dq"]
     kms = {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, n in enumerate(names)}
@@ -175,7 +224,14 @@ def main():
             "traffic": traffic,
             "algorithmic_flops_per_launch": alg_flops[dom],
         },
+        "clock_mhz": clk.summary(),
+        "cus": torch.cuda.get_device_properties(dev).multi_processor_count,
     }
+    cs = out["clock_mhz"]
+    if cs is not None:
+        # The same fraction against the peak at the clock the chip actually ran
+        # (the dense peak scales with the shader clock; 2400 MHz is its maximum).
+        out["roofline"]["frac_at_measured_clock"] = round(achieved / (PEAK_BF16_TFLOPS * cs["mean"] / 2400.0), 4)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_seconds)
