@@ -2,6 +2,9 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
+With --workload, any bf16 workload of seeded_inputs.CONFIGS (forward-only
+ones time the forward alone).
+
 A step is one pass of the whole path over one batch of synthetic inputs
 already resident in HBM: the forward (O, LSE) and the backward (row term,
 dK/dV, dQ).  The default workload is Llama2-7B heads at 32k context
@@ -122,15 +125,16 @@ def main():
     from shifted_sparse_attention_amd import flops as F
 
     wl = CONFIGS[args.workload or HEADLINE]
-    if wl.dtype != "bf16" or not wl.backward:
-        raise SystemExit("bench.py times bf16 forward+backward workloads")
+    if wl.dtype != "bf16":
+        raise SystemExit("bench.py times bf16 workloads")
     B, L, Hq, Hkv, d, G, sh = wl.B, wl.L, wl.Hq, wl.Hkv, wl.d, wl.G, wl.shifted_heads
     rope = (wl.rope_base, wl.rope_orig_len) if wl.rope else None
 
     t0 = time.time()
     x = make_inputs(wl)
     dev = torch.device("cuda:0")
-    tq, tk, tv, tdo = (torch.from_numpy(x[n]).to(torch.bfloat16).to(dev) for n in ("q", "k", "v", "do"))
+    tq, tk, tv = (torch.from_numpy(x[n]).to(torch.bfloat16).to(dev) for n in ("q", "k", "v"))
+    tdo = torch.from_numpy(x["do"]).to(torch.bfloat16).to(dev) if wl.backward else torch.empty_like(tq)
     print(f"# inputs ready in {time.time() - t0:.1f}s: {wl.name}", file=sys.stderr, flush=True)
 
     o = torch.empty_like(tq)
@@ -149,6 +153,8 @@ def main():
         s2.s2attn_fwd_ex(tq, tk, tv, o, lse, B, L, Hq, Hkv, d, G, sh, opts, ws, fws, stream)
         if ev is not None:
             ev[1].record(stream)
+        if not wl.backward:
+            return
         s2.s2attn_bwd_stage_ex(s2.S2ATTN_BWD_STAGE_PRE, *sargs)
         if ev is not None:
             ev[2].record(stream)
@@ -163,7 +169,8 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    n_ev = 5 if wl.backward else 2
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     with ClockSampler() as clk:
@@ -173,7 +180,7 @@ def main():
         end.record(stream)
         torch.cuda.synchronize()
     ms_step = start.elapsed_time(end) / args.steps
-    names = ["fwd", "bwd_pre", "bwd_dkdv", "bwd_dq"]
+    names = ["fwd", "bwd_pre", "bwd_dkdv", "bwd_dq"][:n_ev - 1]
     kms = {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, n in enumerate(names)}
 
     if args.copy_probe_mb:
@@ -183,21 +190,23 @@ def main():
         b.copy_(a)
         torch.cuda.synchronize()
 
-    fl = F.fwd_bwd_flops(B, L, Hq, d, G)
+    fl = F.fwd_bwd_flops(B, L, Hq, d, G) if wl.backward else F.fwd_flops(B, L, Hq, d, G)
     tflops = fl / (ms_step * 1e-3) / 1e12
     unit = float(B) * Hq * L * G * d     # one product over all group-local causal pairs
     alg_flops = {"fwd": 2 * unit, "bwd_dkdv": 4 * unit, "bwd_dq": 1 * unit}
+    alg_flops = {k: v for k, v in alg_flops.items() if k in kms}
     dom = max(alg_flops, key=lambda n: kms[n])
     achieved = alg_flops[dom] / (kms[dom] * 1e-3) / 1e12
 
     traffic = None
-    if os.path.exists(TRAFFIC_FILE):
+    if wl.name == HEADLINE and os.path.exists(TRAFFIC_FILE):   # counters were taken on that workload
         tr = json.load(open(TRAFFIC_FILE))
         if tr.get("source_sha") == kernel_source_sha() and dom in tr.get("kernels", {}):
             traffic = tr["kernels"][dom]["hbm_bytes_per_launch"]
 
+    metric = METRIC if wl.name == HEADLINE else f"S²-Attn {'fwd+bwd' if wl.backward else 'fwd'} TFLOP/s, {wl.name}"
     out = {
-        "metric": METRIC,
+        "metric": metric,
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -240,12 +249,31 @@ def main():
 
 def cpu_baseline(wl, x, seconds):
     """The oracle (fp64 numpy, as it stands) on whole (head, group) units of the
-    same workload, forward + backward, until about `seconds` of CPU time."""
+    same workload, forward + backward, until about `seconds` of CPU time.
+    Forward-only workloads run the oracle's row-at-a-time forward on rows
+    spread over the group instead (a unit there can span the whole context)."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
     from oracle import s2attn as O
     from shifted_sparse_attention_amd import flops as F
+
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                   if i.get("user_api") == "blas"] or [1])
+    if not wl.backward:
+        rng = np.random.default_rng(0)
+        done_rows, fl, t0 = 0, 0.0, time.time()
+        while time.time() - t0 < seconds:
+            rows = sorted(int(i) for i in rng.integers(0, wl.G, 8))
+            h = int(rng.integers(0, wl.Hq))
+            O.sampled_rows_forward(x["q"], x["k"], x["v"], wl.G, wl.shifted_heads, 0, h, 0, rows)
+            fl += sum(4.0 * wl.d * (i + 1) for i in rows)   # 2d per key for Q.K and for P.V
+            done_rows += len(rows)
+        dt = time.time() - t0
+        return {"value": round(fl / dt / 1e12, 5), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+                "sample": f"{done_rows} query rows drawn uniformly over the group, forward in fp64 row by row "
+                          f"({dt:.1f} s); counted FLOPs 4*d per attended key",
+                "seconds": round(dt, 2)}
 
     scale = 1.0 / np.sqrt(wl.d)
     units = [(0, h, g) for g in range(wl.n_groups) for h in (0, wl.Hq - 1, wl.Hq // 2, 1)]
@@ -261,8 +289,6 @@ def cpu_baseline(wl, x, seconds):
             break
     dt = time.time() - t0
     fl = done * F.fwd_bwd_flops(1, wl.G, 1, wl.d, wl.G)   # one unit = one head, one group
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()
-                   if i.get("user_api") == "blas"] or [1])
     return {"value": round(fl / dt / 1e12, 5), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{done} (head, group) units of G={wl.G} rows, forward+backward in fp64 "
                       f"({dt:.1f} s); counted FLOPs as for the GPU",

@@ -283,6 +283,39 @@ def sampled_forward(q, k, v, G, shifted_heads, unit_list, scale=None, rope=None)
     return out
 
 
+def sampled_rows_forward(q, k, v, G, shifted_heads, b, h, g, rows_in_group, scale=None, rope=None):
+    """Forward of chosen query rows of unit (b, h, g), each on its own.
+
+    Row i (in-group index, rolled order) attends to the keys of in-group
+    index 0 .. i of its group: the plain definition, one row at a time, for
+    units too long to run whole (a dense causal pass with G = L).  Returns
+    (original token indices of the rows, o [n, d], lse [n]).
+    """
+    B, L, Hq, d = q.shape
+    r = Hq // k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    members = unit_rows(L, G, Hq, shifted_heads, h, g)
+    theta = rope_angles(L, d, *rope) if rope is not None else None
+    toks, os_, lses = [], [], []
+    for i in rows_in_group:
+        keys = members[:i + 1]
+        qi = np.asarray(q[b, members[i], h], dtype=np.float64)
+        kk = np.asarray(k[b, keys, h // r], dtype=np.float64)
+        vv = np.asarray(v[b, keys, h // r], dtype=np.float64)
+        if theta is not None:
+            qi = rope_rotate(qi[None, None, None, :], theta[members[i]][None])[0, 0, 0]
+            kk = rope_rotate(kk[None, :, None, :], theta[keys])[0, :, 0, :]
+        s = scale * (kk @ qi)
+        m = s.max()
+        e = np.exp(s - m)
+        l = e.sum()
+        toks.append(members[i])
+        lses.append(m + np.log(l))
+        os_.append((e / l) @ vv)
+    return np.array(toks), np.array(os_), np.array(lses)
+
+
 def sampled_kv_backward(q, k, v, do, G, shifted_heads, kv_units, scale=None, rope=None):
     """Gradients for selected (b, kv_head, g) units, whose r query heads share a shift.
 

@@ -1,4 +1,4 @@
-"""The five S2-Attn workloads, with their shapes, dtypes and seeds.
+"""The S2-Attn workloads, with their shapes, dtypes and seeds.
 
 Shapes follow the Llama2 attention heads the LongLoRA pages fine-tune
 (7B: 32 heads of d=128; 70B: 64 query heads sharing 8 KV heads), at the
@@ -8,6 +8,9 @@ nearauto.com article's Table 7 (ablations) attention FLOP shares come out.
 Values are iid N(0, 1): the pages train on PG19 / RedPajama text, which is not
 available here; dense unstructured draws stand in for the activations, and the
 kernels' work does not depend on the values.
+
+The first five are the S2-Attn training shapes; the two `causal` workloads
+are the dense causal inference pass (one group spanning the whole context).
 """
 
 from dataclasses import dataclass, field
@@ -67,6 +70,16 @@ CONFIGS = {
         name="fwdbwd_bf16_L32k_gqa", B=1, L=32768, Hq=64, Hkv=8, d=128, G=8192,
         shifted_heads=32, dtype="bf16", backward=True, seed=5,
         note="forward+backward, Llama2-70B grouped-query shape"),
+    # Dense causal attention (G = L, no shifted heads): the inference pass the
+    # pages run after fine-tuning, where S2-Attn is no longer used.
+    "fwd_bf16_causal_L32k": Workload(
+        name="fwd_bf16_causal_L32k", B=1, L=32768, Hq=32, Hkv=32, d=128, G=32768,
+        shifted_heads=0, dtype="bf16", backward=False, seed=6,
+        note="forward only, full causal attention over 32k tokens (inference)"),
+    "fwd_bf16_causal_L100k": Workload(
+        name="fwd_bf16_causal_L100k", B=1, L=102400, Hq=32, Hkv=32, d=128, G=102400,
+        shifted_heads=0, dtype="bf16", backward=False, seed=7,
+        note="forward only, full causal attention over 100k tokens (inference)"),
 }
 
 # The workload the headline throughput is quoted on: fwd+bwd, Llama2-7B heads, L=32k.

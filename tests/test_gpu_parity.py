@@ -1,10 +1,11 @@
 """GPU parity: libs2attn's HIP kernels against the CPU oracle on seeded inputs.
 
 Small shapes (several tiles, ragged tails, GQA, RoPE, degenerate groups) are
-compared element by element over whole tensors.  The five workloads run at
-full size on the GPU and are compared on the units (one KV head and group,
-with all its query heads) that the oracle recomputes one by one, plus
-properties that hold at any size over every group.
+compared element by element over whole tensors.  The workloads run at full
+size on the GPU and are compared on the units (one KV head and group, with
+all its query heads) that the oracle recomputes one by one, or, where one
+group spans the whole context (dense causal attention), on sampled rows;
+plus properties that hold at any size over every group.
 
 Tolerances: bf16 outputs and gradients rel-Frobenius <= 5e-3 and max-abs <=
 2e-2; fp32 path <= 1e-5 for both.  Where a gradient's magnitude puts half a
@@ -12,6 +13,8 @@ bf16 ulp above 2e-2 (dK, dV of the grouped-query workload reach ~10), parity
 is judged on fp32-stored gradients of the same kernels, and the bf16-stored
 result is held to its rounding floor instead.
 """
+
+import dataclasses
 
 import numpy as np
 import pytest
@@ -234,6 +237,50 @@ def test_workload_fwdbwd_bf16_L32k_gqa():
     _, outs16 = _run_fwdbwd(wl, x, grad_dtype=BF)
     say(" gradients stored in bf16")
     _sampled_parity(wl, x, outs16, units[1:], grads_f32=False, o_lse=False)
+
+
+def _causal_rows(G):
+    """In-group rows to sample: the first, tile edges (32 / 64 / 128 / 256) on
+    both sides, the middle, and the last rows of the group."""
+    edges = {0, 1, 31, 32, 63, 64, 127, 128, 255, 256, 257}
+    return sorted(edges | {G // 2 - 1, G // 2, G - 257, G - 256, G - 129, G - 128, G - 2, G - 1})
+
+
+@pytest.mark.parametrize("name", ["fwd_bf16_causal_L32k", "fwd_bf16_causal_L100k"])
+def test_workload_dense_causal(name):
+    """Dense causal attention (one group spanning the context, no shift), the
+    inference pass: sampled rows of several heads against the oracle, row by
+    row, and every output finite."""
+    wl = CONFIGS[name]
+    say(f"[workload] {wl.name}")
+    x = make_inputs(wl)
+    tq, tk, tv = (dev(x[n], BF) for n in ("q", "k", "v"))
+    o, lse = s2.forward(tq, tk, tv, wl.G, wl.shifted_heads)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())
+    # query 0 sees only itself: o = v exactly
+    assert torch.equal(o[:, 0], tv[:, 0].repeat_interleave(wl.r, dim=1))
+    rows = _causal_rows(wl.G)
+    for h in (0, 13, wl.Hq - 1):
+        toks, ro, rl = O.sampled_rows_forward(x["q"], x["k"], x["v"], wl.G, wl.shifted_heads,
+                                              0, h, 0, rows)
+        tt = torch.from_numpy(toks).cuda()
+        say(f" head {h}: {len(rows)} rows")
+        check("o", host(o[0, tt, h]), ro, BF16_REL_F, BF16_MAX_ABS)
+        check("lse", host(lse[0, h, tt]), rl, BF16_REL_F, BF16_MAX_ABS)
+
+
+@pytest.mark.parametrize("sh", [0, 32])
+def test_shift_counts_full_size(sh):
+    """The 32k training shape with no shifted head (plain short attention) and
+    with every head shifted: sampled units and group sums."""
+    wl = CONFIGS["fwdbwd_bf16_L32k"]
+    say(f"[shift count] {wl.name} shifted_heads={sh}")
+    x = make_inputs(wl)
+    wl2 = dataclasses.replace(wl, shifted_heads=sh, name=f"{wl.name}_sh{sh}")
+    ins, outs = _run_fwdbwd(wl2, x, grad_dtype=torch.float32)
+    _group_sums_hold(wl2, ins[3], outs[3], outs[4], rope=False)
+    _sampled_parity(wl2, x, outs, [(0, 5, 3), (0, 30, 0)], grads_f32=True)
 
 
 # ---------------------------------------------------------------------------

@@ -30,6 +30,7 @@ def _pins(golden_dir):
         P.test_rope_is_complex_rotation,
         P.test_closed_forms,
         P.test_gradient_identities,
+        P.test_sampled_rows_match_explicit_mask,
     ]
 
 
@@ -54,6 +55,10 @@ MUTATIONS = [
     ("rope_rotate_transpose", "g1 * c + g2 * s, -g1 * s + g2 * c", "g1 * c - g2 * s, g1 * s + g2 * c"),
     ("rope_angles", "pos = np.arange(L, dtype=np.float64) * (float(orig_len) / float(L))",
      "pos = np.arange(L, dtype=np.float64)"),
+    ("sampled_rows_forward", "keys = members[:i + 1]", "keys = members[:i + 2]"),
+    ("sampled_rows_forward", "s = scale * (kk @ qi)", "s = kk @ qi"),
+    ("sampled_rows_forward", "kk = rope_rotate(kk[None, :, None, :], theta[keys])[0, :, 0, :]",
+     "kk = rope_rotate(kk[None, :, None, :], theta[keys][::-1])[0, :, 0, :]"),
     ("rope_angles", "(-2.0 * np.arange(d // 2, dtype=np.float64) / d)",
      "(-1.0 * np.arange(d // 2, dtype=np.float64) / d)"),
 ]

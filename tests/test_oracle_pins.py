@@ -367,6 +367,23 @@ def test_sampled_units_match_full():
                 assert np.allclose(dq[b, rows, h], x, atol=1e-12)
 
 
+def test_sampled_rows_match_explicit_mask():
+    """Row-at-a-time forward (used where a unit spans a whole long context)
+    against the explicit-mask form, including the diagonal row and rows of a
+    shifted head whose group wraps around the sequence end."""
+    rng = np.random.default_rng(93)
+    for (L, G, Hq, Hkv, d, sh, rope) in ((24, 24, 2, 1, 8, 0, None), (32, 8, 4, 2, 8, 2, None),
+                                         (32, 32, 2, 2, 8, 0, (100.0, 8)), (24, 8, 2, 2, 4, 1, (50.0, 6))):
+        q, k, v = qkv(1, L, Hq, Hkv, d, rng=rng)
+        o, lse = O.forward_dense(q, k, v, G, sh, rope=rope)
+        for h in range(Hq):
+            for g in range(L // G):
+                rows_in = [0, 1, G // 2, G - 1]
+                toks, og, lg = O.sampled_rows_forward(q, k, v, G, sh, 0, h, g, rows_in, rope=rope)
+                assert np.allclose(og, o[0, toks, h], atol=1e-12), (L, G, sh, h, g)
+                assert np.allclose(lg, lse[0, h, toks], atol=1e-12), (L, G, sh, h, g)
+
+
 def test_invalid_arguments():
     q, k, v = qkv(1, 12, 2, 2, 4)
     with pytest.raises(ValueError):
