@@ -236,11 +236,6 @@ def main():
         "clock_mhz": clk.summary(),
         "cus": torch.cuda.get_device_properties(dev).multi_processor_count,
     }
-    cs = out["clock_mhz"]
-    if cs is not None:
-        # The same fraction against the peak at the clock the chip actually ran
-        # (the dense peak scales with the shader clock; 2400 MHz is its maximum).
-        out["roofline"]["frac_at_measured_clock"] = round(achieved / (PEAK_BF16_TFLOPS * cs["mean"] / 2400.0), 4)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_seconds)
