@@ -3,7 +3,8 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 With --workload, any bf16 workload of seeded_inputs.CONFIGS (forward-only
-ones time the forward alone).
+ones time the forward alone) or of seeded_inputs.BLOCK_CONFIGS (the attention
+block around S2-Attn: LoRA Q/K/V/O projections, RoPE-PI, forward+backward).
 
 A step is one pass of the whole path over one batch of synthetic inputs
 already resident in HBM: the forward (O, LSE) and the backward (row term,
@@ -120,10 +121,12 @@ def main():
     import torch
 
     import shifted_sparse_attention_amd as s2
-    from seeded_inputs import CONFIGS, make_inputs
+    from seeded_inputs import BLOCK_CONFIGS, CONFIGS, make_inputs
     from seeded_inputs.configs import HEADLINE
     from shifted_sparse_attention_amd import flops as F
 
+    if args.workload in BLOCK_CONFIGS:
+        return bench_block(args, BLOCK_CONFIGS[args.workload])
     wl = CONFIGS[args.workload or HEADLINE]
     if wl.dtype != "bf16":
         raise SystemExit("bench.py times bf16 workloads")
@@ -240,6 +243,129 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def bench_block(args, wl):
+    """The attention block (LoRA Q/K/V/O on hipBLASLt, RoPE-PI, S2-Attn): one
+    step is its forward and backward."""
+    import numpy as np
+    import torch
+
+    import shifted_sparse_attention_amd as s2
+    from seeded_inputs import make_block_inputs
+    from shifted_sparse_attention_amd import flops as F
+
+    t0 = time.time()
+    inp = make_block_inputs(wl)
+    dev = torch.device("cuda:0")
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(torch.bfloat16).to(dev)
+
+    x, dy = up(inp["x"]), up(inp["dy"])
+    params = {k: up(v) for k, v in inp["params"].items()}
+    print(f"# inputs ready in {time.time() - t0:.1f}s: {wl.name}", file=sys.stderr, flush=True)
+    rope = (wl.rope_base, wl.rope_orig_len) if wl.rope else None
+    blk = s2.block.Block(wl.B, wl.L, wl.Hq, wl.Hkv, wl.d, wl.G, wl.shifted_heads, wl.lora_rank,
+                         wl.lora_scale, rope=rope)
+    wsb = blk.workspace(1, dev)          # the backward's workspace covers the forward's
+    stream = torch.cuda.current_stream()
+    saved = blk.alloc_saved(dev)
+    y = torch.empty_like(x)
+    grads = {"dx": torch.empty_like(x)}
+    for name, shp in s2.block.param_shapes(wl.Hq, wl.Hkv, wl.d, wl.lora_rank).items():
+        if name[0] in "ab":
+            grads["d" + name] = torch.empty(shp, dtype=torch.float32, device=dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        s2.s2block_fwd(blk.cfg, x, params, y, saved, wsb[0], wsb[1], stream)
+        if ev is not None:
+            ev[1].record(stream)
+        s2.s2block_bwd(blk.cfg, x, params, saved, dy, grads, wsb[0], wsb[1], stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with ClockSampler() as clk:
+        start.record(stream)
+        for i in range(args.steps):
+            step(evs[i])
+        end.record(stream)
+        torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / args.steps
+    kms = {"block_fwd": float(np.mean([e[0].elapsed_time(e[1]) for e in evs])),
+           "block_bwd": float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))}
+    ffl, bfl = F.block_flops(wl.B, wl.L, wl.Hq, wl.Hkv, wl.d, wl.G, wl.lora_rank)
+    att = F.fwd_bwd_flops(wl.B, wl.L, wl.Hq, wl.d, wl.G)
+    tflops = (ffl + bfl) / (ms_step * 1e-3) / 1e12
+    dom = max(kms, key=kms.get)
+    dom_fl = ffl if dom == "block_fwd" else bfl
+    achieved = dom_fl / (kms[dom] * 1e-3) / 1e12
+    out = {
+        "metric": f"Attention block (LoRA Q/K/V/O + RoPE-PI + S²-Attn) fwd+bwd TFLOP/s, {wl.name}",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (random weights)",
+        "config": {"workload": wl.name, "B": wl.B, "L": wl.L, "Hq": wl.Hq, "Hkv": wl.Hkv, "d": wl.d,
+                   "G": wl.G, "shifted_heads": wl.shifted_heads, "lora_rank": wl.lora_rank,
+                   "rope": bool(wl.rope), "seed": wl.seed, "parallelism": "single GPU"},
+        "pct_of_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "kernels_ms": {k: round(v, 4) for k, v in kms.items()},
+        "attention_flop_share": round(att / (ffl + bfl), 4),
+        # The block's launches sit inside one C call each; the dominant unit
+        # timed with events on its stream is the forward or the backward call.
+        "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "algorithmic_flops_per_launch": dom_fl},
+        "clock_mhz": clk.summary(),
+        "cus": torch.cuda.get_device_properties(dev).multi_processor_count,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_block(wl, inp, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_block(wl, inp, seconds):
+    """The block oracle (fp64 numpy) on the same workload: y at a few tokens at
+    a time, each from the definition (every head's projections of the causal
+    prefix of its group, attention, the output projection), until about
+    `seconds` of CPU time.  FLOPs are those the oracle performs."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import block as OB
+    from oracle import s2attn as O
+
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                   if i.get("user_api") == "blas"] or [1])
+    rng = np.random.default_rng(0)
+    Dm, d, r = wl.Hq * wl.d, wl.d, wl.lora_rank
+    rope = (wl.rope_base, wl.rope_orig_len) if wl.rope else None
+    fl, done, t0 = 0.0, 0, time.time()
+    while time.time() - t0 < seconds:
+        toks = [int(t) for t in rng.integers(0, wl.L, 2)]
+        OB.sampled_forward_tokens(inp["x"], inp["params"], wl.G, wl.shifted_heads, wl.Hq, wl.Hkv,
+                                  wl.d, wl.lora_scale, 0, toks, rope=rope)
+        for h in range(wl.Hq):
+            s = O.head_shift(h, wl.Hq, wl.G, wl.shifted_heads)
+            rows = max(int(O.original_to_rolled(t, wl.L, s)) % wl.G for t in toks) + 1
+            fl += 2.0 * rows * Dm * 3 * (d + r) + 2.0 * rows * r * 3 * d   # q, k, v slices + LoRA
+            fl += sum(4.0 * d * (int(O.original_to_rolled(t, wl.L, s)) % wl.G + 1) for t in toks)
+        fl += len(toks) * (2.0 * Dm * Dm + 2.0 * r * (2 * Dm))            # output projection
+        done += len(toks)
+    dt = time.time() - t0
+    return {"value": round(fl / dt / 1e12, 5), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"block output y at {done} tokens of the same workload, fp64, each from its "
+                      f"heads' causal group prefixes ({dt:.1f} s); forward only",
+            "seconds": round(dt, 2)}
 
 
 def cpu_baseline(wl, x, seconds):

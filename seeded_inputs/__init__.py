@@ -5,7 +5,8 @@ the attention arithmetic: the GPU path and the CPU oracle each implement the
 method on their own and meet only here, on identical input values.
 """
 
-from .configs import CONFIGS, Workload, workload
-from .gen import bf16_round, bf16_bits, make_inputs
+from .configs import BLOCK_CONFIGS, CONFIGS, BlockWorkload, Workload, workload
+from .gen import bf16_bits, bf16_round, make_block_inputs, make_inputs
 
-__all__ = ["CONFIGS", "Workload", "workload", "bf16_round", "bf16_bits", "make_inputs"]
+__all__ = ["BLOCK_CONFIGS", "CONFIGS", "BlockWorkload", "Workload", "workload", "bf16_round",
+           "bf16_bits", "make_block_inputs", "make_inputs"]

@@ -82,6 +82,41 @@ CONFIGS = {
         note="forward only, full causal attention over 100k tokens (inference)"),
 }
 
+@dataclass(frozen=True)
+class BlockWorkload:
+    """One Llama-style attention block around S2-Attn with LoRA on Q, K, V, O."""
+    name: str
+    B: int
+    L: int
+    Hq: int
+    Hkv: int
+    d: int
+    G: int
+    shifted_heads: int
+    lora_rank: int
+    lora_scale: float
+    seed: int
+    rope: bool = False
+    rope_base: float = 10000.0
+    rope_orig_len: int = 4096
+    note: str = field(default="", compare=False)
+
+    @property
+    def Dm(self) -> int:
+        return self.Hq * self.d
+
+
+BLOCK_CONFIGS = {
+    "block_bf16_L1k": BlockWorkload(
+        name="block_bf16_L1k", B=1, L=1024, Hq=4, Hkv=2, d=128, G=256, shifted_heads=2,
+        lora_rank=8, lora_scale=2.0, seed=11, rope=True, rope_orig_len=256,
+        note="small block: GQA, RoPE position interpolation 256 -> 1024"),
+    "block_bf16_L32k": BlockWorkload(
+        name="block_bf16_L32k", B=1, L=32768, Hq=32, Hkv=32, d=128, G=8192, shifted_heads=16,
+        lora_rank=8, lora_scale=2.0, seed=12, rope=True, rope_orig_len=4096,
+        note="Llama2-7B attention block at 32k, RoPE position interpolation 4k -> 32k"),
+}
+
 # The workload the headline throughput is quoted on: fwd+bwd, Llama2-7B heads, L=32k.
 HEADLINE = "fwdbwd_bf16_L32k"
 

@@ -49,3 +49,33 @@ def make_inputs(wl, seed=None, with_grad=None):
             x = bf16_round(x)
         out[name] = x
     return out
+
+
+BLOCK_PARAM_ORDER = ("wq", "wk", "wv", "wo", "aq", "ak", "av", "ao", "bq", "bk", "bv", "bo")
+
+
+def make_block_inputs(wl, seed=None, scale_up=0.25):
+    """x, dy and the block's weights for a BlockWorkload, rounded to bf16.
+
+    Draw order from one default_rng(seed) stream: x, then the weights in
+    BLOCK_PARAM_ORDER, then dy; all standard normals in float32.  A weight
+    with fan-in n is scaled by 1/sqrt(n) before rounding, so q, k, v and y are
+    O(1).  The LoRA up-projections (B) are random too, so the adapter path
+    carries signal (they would start at zero in training), at `scale_up` of
+    that scale: the adapters perturb the frozen projections rather than
+    dominate them.
+    """
+    rng = np.random.default_rng(wl.seed if seed is None else seed)
+    Dm, Nq, Nkv, r = wl.Hq * wl.d, wl.Hq * wl.d, wl.Hkv * wl.d, wl.lora_rank
+    shapes = {"wq": (Nq, Dm), "wk": (Nkv, Dm), "wv": (Nkv, Dm), "wo": (Dm, Nq),
+              "aq": (r, Dm), "ak": (r, Dm), "av": (r, Dm), "ao": (r, Nq),
+              "bq": (Nq, r), "bk": (Nkv, r), "bv": (Nkv, r), "bo": (Dm, r)}
+    out = {"x": bf16_round(rng.standard_normal((wl.B, wl.L, Dm), dtype=np.float32))}
+    p = {}
+    for name in BLOCK_PARAM_ORDER:
+        shp = shapes[name]
+        w = rng.standard_normal(shp, dtype=np.float32) * np.float32(1.0 / np.sqrt(shp[1]))
+        p[name] = bf16_round(w * np.float32(scale_up if name[0] == "b" else 1.0))
+    out["params"] = p
+    out["dy"] = bf16_round(rng.standard_normal((wl.B, wl.L, Dm), dtype=np.float32))
+    return out

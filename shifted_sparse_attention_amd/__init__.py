@@ -18,7 +18,9 @@ from ._lib import (  # noqa: F401
     LIB_PATH, S2ATTN_BF16, S2ATTN_BWD_STAGE_DKDV, S2ATTN_BWD_STAGE_DQ, S2ATTN_BWD_STAGE_PRE, S2ATTN_ERR_HIP, S2ATTN_ERR_INVALID_ARG, S2ATTN_ERR_UNSUPPORTED,
     S2ATTN_ERR_WORKSPACE, S2ATTN_F32, S2ATTN_OK, S2AttnError, lib, s2attn_bwd, s2attn_bwd_ex, s2attn_bwd_stage_ex,
     s2attn_fwd, s2attn_fwd_ex, s2attn_opts, s2attn_opts_init, s2attn_status_string,
-    s2attn_version, s2attn_workspace_size)
+    s2attn_version, s2attn_workspace_size, s2block_bwd, s2block_config, s2block_config_init,
+    s2block_fwd, s2block_grads, s2block_params, s2block_saved, s2block_workspace_size)
+from . import block  # noqa: F401,E402
 
 _DT = {torch.bfloat16: S2ATTN_BF16, torch.float32: S2ATTN_F32}
 

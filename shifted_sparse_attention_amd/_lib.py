@@ -46,6 +46,34 @@ class s2attn_opts(ctypes.Structure):
     ]
 
 
+class s2block_config(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("B", ctypes.c_int32), ("L", ctypes.c_int32), ("Hq", ctypes.c_int32),
+        ("Hkv", ctypes.c_int32), ("d", ctypes.c_int32),
+        ("G", ctypes.c_int32), ("shifted_heads", ctypes.c_int32),
+        ("lora_rank", ctypes.c_int32),
+        ("lora_scale", ctypes.c_float),
+        ("rope", ctypes.c_int32),
+        ("rope_base", ctypes.c_float),
+        ("rope_orig_len", ctypes.c_int32),
+    ]
+
+
+class s2block_params(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("wq", "wk", "wv", "wo", "aq", "ak", "av", "ao", "bq", "bk", "bv", "bo")]
+
+
+class s2block_saved(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("q", "k", "v", "attn", "lse", "u")]
+
+
+class s2block_grads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("dx", "daq", "dak", "dav", "dao", "dbq", "dbk", "dbv", "dbo")]
+
+
 _lib = None
 
 _vp, _ci, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
@@ -60,6 +88,13 @@ _SIGS = {
                             + [ctypes.POINTER(s2attn_opts), _vp, _sz, _vp]),
     "s2attn_status_string": (ctypes.c_char_p, [_ci]),
     "s2attn_version": (_ci, []),
+    "s2block_config_init": (s2block_config, []),
+    "s2block_workspace_size": (_sz, [_ci, ctypes.POINTER(s2block_config)]),
+    "s2block_fwd": (_ci, [ctypes.POINTER(s2block_config), _vp, ctypes.POINTER(s2block_params), _vp,
+                          ctypes.POINTER(s2block_saved), _vp, _sz, _vp]),
+    "s2block_bwd": (_ci, [ctypes.POINTER(s2block_config), _vp, ctypes.POINTER(s2block_params),
+                          ctypes.POINTER(s2block_saved), _vp, ctypes.POINTER(s2block_grads), _vp,
+                          _sz, _vp]),
 }
 
 
@@ -175,3 +210,30 @@ def s2attn_status_string(status):
 
 def s2attn_version():
     return int(lib().s2attn_version())
+
+
+def s2block_config_init():
+    return lib().s2block_config_init()
+
+
+def s2block_workspace_size(is_bwd, cfg):
+    return int(lib().s2block_workspace_size(int(is_bwd), ctypes.byref(cfg)))
+
+
+def _struct(cls, d):
+    return cls(**{name: _ptr(d[name]) for name, _ in cls._fields_})
+
+
+def s2block_fwd(cfg, x, params, y, saved, ws, ws_bytes, stream=None):
+    """params / saved: dicts of tensors keyed by the struct field names."""
+    p, sv = _struct(s2block_params, params), _struct(s2block_saved, saved)
+    _check(lib().s2block_fwd(ctypes.byref(cfg), _ptr(x), ctypes.byref(p), _ptr(y), ctypes.byref(sv),
+                             _ptr(ws), int(ws_bytes), _stream(stream)), "s2block_fwd")
+
+
+def s2block_bwd(cfg, x, params, saved, dy, grads, ws, ws_bytes, stream=None):
+    p, sv = _struct(s2block_params, params), _struct(s2block_saved, saved)
+    g = _struct(s2block_grads, grads)
+    _check(lib().s2block_bwd(ctypes.byref(cfg), _ptr(x), ctypes.byref(p), ctypes.byref(sv), _ptr(dy),
+                             ctypes.byref(g), _ptr(ws), int(ws_bytes), _stream(stream)),
+           "s2block_bwd")

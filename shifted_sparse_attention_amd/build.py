@@ -79,8 +79,10 @@ def build(verbose=False, extra_flags=()):
                 print("\n".join(errs), flush=True)
             objs.append(obj)
         tmp_lib = LIB_PATH + ".tmp"
+        # hipBLASLt (the attention block's projection GEMMs) from the same
+        # directory as the HIP runtime, so both come from one ROCm release.
         cmd = [clangxx, "-shared", "-fPIC", *objs, "-o", tmp_lib,
-               f"-L{rt}", "-l:libamdhip64.so", f"-Wl,-rpath,{rt}",
+               f"-L{rt}", "-l:libamdhip64.so", "-l:libhipblaslt.so", f"-Wl,-rpath,{rt}",
                f"-Wl,-rpath,{os.path.join(ROCM, 'lib')}", "-Wl,--no-undefined",
                "-Wl,-soname," + LIB_NAME]
         if verbose:

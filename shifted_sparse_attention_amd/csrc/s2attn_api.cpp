@@ -233,6 +233,21 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const f
 
 }  // namespace
 
+namespace s2 {
+
+int attention_config_status(int is_bwd, int B, int L, int Hq, int Hkv, int d, int G,
+                            int shifted_heads, const s2attn_opts* opts) {
+    int st = check_sizes(B, L, Hq, Hkv, d, G, shifted_heads);
+    if (st) return st;
+    Resolved r;
+    st = resolve_opts(opts, d, &r);
+    if (st) return st;
+    if (is_bwd && shifted_heads % (Hq / Hkv) != 0) return S2ATTN_ERR_UNSUPPORTED;
+    return S2ATTN_OK;
+}
+
+}  // namespace s2
+
 extern "C" {
 
 void s2attn_opts_init(s2attn_opts* opts) {

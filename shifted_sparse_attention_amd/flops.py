@@ -62,3 +62,27 @@ def llama2_7b_attention_share(L, keys_per_query, dims=LLAMA2_7B):
     linear = 2.0 * (nl * (4 * h * h + 3 * h * f) + h * V)
     attn = nl * 4.0 * keys_per_query * h
     return attn / (attn + linear)
+
+
+def block_flops(B, L, Hq, Hkv, d, G, r):
+    """Counted FLOPs of one attention block (LoRA Q/K/V/O, frozen W) forward and backward.
+
+    Each product is 2 * rows * fan_in * fan_out.  Forward: the projections
+    x W^T (Q, K, V) and attn Wo^T, the LoRA down (x A^T, attn Ao^T) and up
+    (u B^T) products, and S2-Attn.  Backward: dattn = dy Wo and dx = sum dz W
+    (no dW: W is frozen), the LoRA factor gradients and the LoRA terms of
+    dattn and dx, and the S2-Attn backward.  Returns (forward, backward).
+    """
+    M, Dm, Nq, Nkv = float(B) * L, Hq * d, Hq * d, Hkv * d
+    n_qkv = Nq + 2 * Nkv
+    fwd = (2 * M * Dm * n_qkv + 2 * M * Nq * Dm          # x W^T, attn Wo^T
+           + 2 * M * r * (3 * Dm + Nq)                   # x A^T (q, k, v), attn Ao^T
+           + 2 * M * r * (n_qkv + Dm)                    # u B^T
+           + fwd_flops(B, L, Hq, d, G))
+    bwd = (2 * M * Nq * Dm + 2 * M * Dm * n_qkv          # dy Wo, dz W
+           + 2 * M * r * (Dm + n_qkv)                    # t = dz B
+           + 2 * M * r * (Dm + n_qkv)                    # dB = dz^T u
+           + 2 * M * r * (Nq + 3 * Dm)                   # dA = t^T (attn | x)
+           + 2 * M * r * (Nq + 3 * Dm)                   # t A into dattn, dx
+           + bwd_flops(B, L, Hq, d, G))
+    return fwd, bwd

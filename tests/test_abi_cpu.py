@@ -16,15 +16,19 @@ from shifted_sparse_attention_amd import _lib as L
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "s2attn.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+                 if f.endswith(".h"))
 
 FAKE = 0x10000  # 16-byte aligned, never dereferenced
 MIS = 0x10008   # misaligned
 
 
-def declared_functions():
-    src = open(HEADER).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(s2attn_\w+)\s*\(", src)))
+def declared_functions(headers=None):
+    names = set()
+    for h in headers or HEADERS:
+        src = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(s2(?:attn|block)_\w+)\s*\(", src))
+    return sorted(names)
 
 
 def test_library_loads_and_exports_header_symbols():
@@ -171,10 +175,11 @@ def test_python_wrappers_raise_named_errors():
 
 
 def test_header_documents_each_entry_point():
-    src = open(HEADER).read()
-    for name in declared_functions():
-        m = re.search(r"(\*/)\s*(?:const\s+)?[\w\s\*]*\b" + name + r"\s*\(", src)
-        assert m, f"{name} is not directly preceded by a comment"
+    for h in HEADERS:
+        src = open(h).read()
+        for name in declared_functions([h]):
+            m = re.search(r"(\*/)\s*(?:const\s+)?[\w\s\*]*\b" + name + r"\s*\(", src)
+            assert m, f"{name} is not directly preceded by a comment in {h}"
 
 
 def test_bwd_stage_checks():
@@ -187,3 +192,66 @@ def test_bwd_stage_checks():
     st = L.lib().s2attn_bwd_stage_ex(L.S2ATTN_BWD_STAGE_DKDV, *([FAKE] * 9), 1, 256, 4, 4, 64, 64,
                                      2, ctypes.byref(o), None, 0, None)
     assert st == WS
+
+
+def _block_cfg(**kw):
+    c = s2.s2block_config_init()
+    for k, v in dict(B=1, L=256, Hq=4, Hkv=2, d=64, G=64, shifted_heads=2).items():
+        setattr(c, k, v)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+BLOCK_PARAMS = {n: FAKE for n in ("wq", "wk", "wv", "wo", "aq", "ak", "av", "ao", "bq", "bk", "bv", "bo")}
+BLOCK_SAVED = {n: FAKE for n in ("q", "k", "v", "attn", "lse", "u")}
+BLOCK_GRADS = {n: FAKE for n in ("dx", "daq", "dak", "dav", "dao", "dbq", "dbk", "dbv", "dbo")}
+
+
+def _block_fwd(cfg, ws=FAKE, ws_bytes=None, params=None, saved=None, x=FAKE):
+    n = s2.s2block_workspace_size(0, cfg) if ws_bytes is None else ws_bytes
+    p = L._struct(L.s2block_params, params or BLOCK_PARAMS)
+    sv = L._struct(L.s2block_saved, saved or BLOCK_SAVED)
+    return L.lib().s2block_fwd(ctypes.byref(cfg), x, ctypes.byref(p), FAKE, ctypes.byref(sv), ws, n, None)
+
+
+def _block_bwd(cfg, ws=FAKE, ws_bytes=None, grads=None):
+    n = s2.s2block_workspace_size(1, cfg) if ws_bytes is None else ws_bytes
+    p = L._struct(L.s2block_params, BLOCK_PARAMS)
+    sv = L._struct(L.s2block_saved, BLOCK_SAVED)
+    g = L._struct(L.s2block_grads, grads or BLOCK_GRADS)
+    return L.lib().s2block_bwd(ctypes.byref(cfg), FAKE, ctypes.byref(p), ctypes.byref(sv), FAKE,
+                               ctypes.byref(g), ws, n, None)
+
+
+def test_block_config_defaults_and_workspace():
+    c = s2.s2block_config_init()
+    assert c.struct_size == ctypes.sizeof(L.s2block_config)
+    assert c.lora_rank == 8 and c.lora_scale == 2.0 and c.rope == 0
+    assert c.rope_base == 10000.0 and c.rope_orig_len == 4096
+    cfg = _block_cfg()
+    f, b = s2.s2block_workspace_size(0, cfg), s2.s2block_workspace_size(1, cfg)
+    assert f >= 32 << 20 and b > f                     # hipBLASLt slice, then backward scratch
+    assert s2.s2block_workspace_size(0, _block_cfg(L=250)) == 0   # L % G != 0
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(struct_size=4), INV), (dict(lora_rank=0), INV), (dict(lora_rank=72), INV),
+    (dict(lora_rank=4), INV), (dict(lora_rank=12), INV),
+    (dict(lora_scale=float("inf")), INV), (dict(G=48), INV), (dict(d=96), UNS),
+    (dict(Hq=8, Hkv=2, shifted_heads=3), UNS), (dict(rope=1, rope_base=0.5), INV),
+])
+def test_block_config_checks(kw, want):
+    assert _block_fwd(_block_cfg(**kw)) == want if "shifted_heads" not in kw else True
+    assert _block_bwd(_block_cfg(**kw)) == want
+
+
+def test_block_pointer_and_workspace_checks():
+    cfg = _block_cfg()
+    assert _block_fwd(cfg, x=None) == INV
+    assert _block_fwd(cfg, params=dict(BLOCK_PARAMS, bo=None)) == INV
+    assert _block_fwd(cfg, saved=dict(BLOCK_SAVED, u=MIS)) == INV
+    assert _block_fwd(cfg, ws=None) == WS
+    assert _block_fwd(cfg, ws_bytes=s2.s2block_workspace_size(0, cfg) - 1) == WS
+    assert _block_bwd(cfg, grads=dict(BLOCK_GRADS, dbq=None)) == INV
+    assert _block_bwd(cfg, ws_bytes=1024) == WS

@@ -79,3 +79,44 @@ def test_mutation_is_caught(fname, orig, mut, monkeypatch, golden_dir):
             caught.append(pin)
             break
     assert caught, f"no pin caught the mutation in {fname}: {mut!r}"
+
+
+# Mutations of the attention-block oracle, against its own pins.
+from oracle import block as OB  # noqa: E402
+from tests import test_block_oracle as BP  # noqa: E402
+
+BLOCK_PINS = [
+    lambda: BP.test_block_matches_torch_autograd(1, 24, 4, 2, 8, 8, 2, 3),
+    BP.test_lora_merges_into_weight,
+    BP.test_zero_up_projection_has_zero_down_gradient,
+    BP.test_finite_differences_with_rope,
+    BP.test_sampled_tokens_match_full_forward,
+]
+
+BLOCK_MUTATIONS = [
+    ("lora_proj", "s * ((X @ A.T) @ Bm.T)", "((X @ A.T) @ Bm.T)"),
+    ("lora_proj_backward", "dX = dY @ W + s * (t @ A)", "dX = dY @ W"),
+    ("lora_proj_backward", "dA = s * (t.T @ X)", "dA = s * (t.T @ dY[:, :X.shape[1]])"),
+    ("lora_proj_backward", "dB = s * (dY.T @ (X @ A.T))", "dB = dY.T @ (X @ A.T)"),
+    ("backward", "dx += dX", "dx = dX"),
+    ("forward", 'k = lora_proj(X, p["wk"], p["ak"], p["bk"], s)', 'k = lora_proj(X, p["wk"], p["aq"][:, :], p["bk"], s)'),
+    ("sampled_forward_tokens", "attn[n, sq] = (e / e.sum()) @ vg[:i + 1]", "attn[n, sq] = (e / e.sum()) @ vg[:i + 1] * 1.0001"),
+]
+
+
+@pytest.mark.parametrize("fname,orig,mut", BLOCK_MUTATIONS,
+                         ids=[f"block.{m[0]}:{i}" for i, m in enumerate(BLOCK_MUTATIONS)])
+def test_block_mutation_is_caught(fname, orig, mut, monkeypatch):
+    src = inspect.getsource(getattr(OB, fname))
+    assert orig in src, f"mutation text not found in {fname}"
+    ns = dict(vars(OB))
+    exec(src.replace(orig, mut), ns)
+    monkeypatch.setattr(OB, fname, ns[fname])
+    caught = False
+    for pin in BLOCK_PINS:
+        try:
+            pin()
+        except (AssertionError, ValueError):
+            caught = True
+            break
+    assert caught, f"no pin caught the mutation in {fname}: {mut!r}"
