@@ -59,26 +59,36 @@ __device__ __forceinline__ void rope_cs(const Params& p, int t, int c, float* cs
     *cs = __builtin_amdgcn_cosf(x);
 }
 
-// Rotated copies of q and k (bf16 in, bf16 out), one thread per channel pair.
+// Rotated copies of q and k (bf16 in, bf16 out).  A thread turns 8 channel
+// pairs: 16 bytes from each half of the row in, 16 bytes to each half out.
 template <int D>
 __global__ __launch_bounds__(256) void rope_prepass_kernel(Params p, bf16* qo, bf16* ko,
                                                            long q_rows, long k_rows) {
     constexpr int HALF = D / 2;
-    constexpr int RPB = 256 / HALF;
-    const long row = (long)blockIdx.x * RPB + threadIdx.x / HALF;
-    const int c = threadIdx.x % HALF;
+    constexpr int TPR = HALF / 8;  // threads per row
+    const long gid = (long)blockIdx.x * 256 + threadIdx.x;
+    const long row = gid / TPR;
+    const int c0 = (int)(gid % TPR) * 8;
     if (row >= q_rows + k_rows) return;
     const bool is_q = row < q_rows;
     const long r = is_q ? row : row - q_rows;
     const int H = is_q ? p.Hq : p.Hkv;
     const int t = (int)((r / H) % p.L);
-    const bf16* src = static_cast<const bf16*>(is_q ? p.q : p.k) + r * D;
-    bf16* dst = (is_q ? qo : ko) + r * D;
-    float cs, sn;
-    rope_cs(p, t, c, &cs, &sn);
-    const float x1 = (float)src[c], x2 = (float)src[c + HALF];
-    dst[c] = (bf16)(x1 * cs - x2 * sn);
-    dst[c + HALF] = (bf16)(x1 * sn + x2 * cs);
+    const bf16* src = static_cast<const bf16*>(is_q ? p.q : p.k) + r * D + c0;
+    bf16* dst = (is_q ? qo : ko) + r * D + c0;
+    const bf16x8 a = *reinterpret_cast<const bf16x8*>(src);
+    const bf16x8 b = *reinterpret_cast<const bf16x8*>(src + HALF);
+    bf16x8 oa, ob;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        float cs, sn;
+        rope_cs(p, t, c0 + i, &cs, &sn);
+        const float x1 = (float)a[i], x2 = (float)b[i];
+        oa[i] = (bf16)(x1 * cs - x2 * sn);
+        ob[i] = (bf16)(x1 * sn + x2 * cs);
+    }
+    *reinterpret_cast<bf16x8*>(dst) = oa;
+    *reinterpret_cast<bf16x8*>(dst + HALF) = ob;
 }
 
 // ---------------------------------------------------------------------------
@@ -714,8 +724,8 @@ hipError_t launch_bwd_pre(const Params& p, int f32_io, hipStream_t st) {
 
 hipError_t launch_rope_prepass(const Params& p, void* q_out, void* k_out, hipStream_t st) {
     const long q_rows = (long)p.B * p.L * p.Hq, k_rows = (long)p.B * p.L * p.Hkv;
-    const int rpb = 256 / (p.d / 2);
-    const long blocks = (q_rows + k_rows + rpb - 1) / rpb;
+    const long threads = (q_rows + k_rows) * (p.d / 16);  // 8 channel pairs per thread
+    const long blocks = (threads + 255) / 256;
     if (p.d == 128)
         hipLaunchKernelGGL(rope_prepass_kernel<128>, dim3(blocks), dim3(256), 0, st, p,
                            static_cast<bf16*>(q_out), static_cast<bf16*>(k_out), q_rows, k_rows);
