@@ -35,14 +35,17 @@ PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwdbwd_bf16_L32k.json")
 
 
+# The sources that define the attention kernels the stored counters describe.
+KERNEL_SOURCES = ("s2_device.h", "s2_params.h", "s2attn_fwd.hip", "s2attn_bwd.hip")
+
+
 def kernel_source_sha():
-    """Hash of the kernel sources, to tell whether stored counters are current."""
+    """Hash of the attention kernels' sources, to tell whether stored counters are current."""
     csrc = os.path.join(ROOT, "shifted_sparse_attention_amd", "csrc")
     h = hashlib.sha256()
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".h", ".cpp")):
-            h.update(f.encode())
-            h.update(open(os.path.join(csrc, f), "rb").read())
+    for f in KERNEL_SOURCES:
+        h.update(f.encode())
+        h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
 
