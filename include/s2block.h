@@ -63,7 +63,7 @@ typedef struct s2block_saved {
     void *q, *k, *v;  /* pre-RoPE projections */
     void *attn;       /* attention output [B, L, Hq, d] */
     float *lse;       /* [B, Hq, L] */
-    void *u;          /* [B L, 4 r] bf16: x Aq^T | x Ak^T | x Av^T | attn Ao^T */
+    void *u;          /* [B L, 4 r] bf16, s times: x Aq^T | x Ak^T | x Av^T | attn Ao^T */
 } s2block_saved;
 
 typedef struct s2block_grads {

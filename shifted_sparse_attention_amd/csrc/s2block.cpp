@@ -17,6 +17,7 @@
 #include "s2_params.h"
 #include "s2attn.h"
 #include "s2block.h"
+#include "s2block_kernels.h"
 
 namespace {
 
@@ -24,6 +25,8 @@ constexpr size_t kAlign = 256;
 constexpr size_t kLtWorkspace = 32u << 20;  // hipBLASLt scratch slice of the caller's workspace
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+// GEMM depths are padded to whole 64-wide K steps (zero columns against zero rows).
+int64_t kpad(int64_t k) { return (k + 63) / 64 * 64; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // ---------------------------------------------------------------------------
@@ -180,16 +183,26 @@ int check_config(const s2block_config* c, int is_bwd, s2attn_opts* att, Dims* dm
     return S2ATTN_OK;
 }
 
-// Workspace: [attention | hipBLASLt | A_cat (3r x Dm bf16) | backward scratch].
+// Workspace: [attention | hipBLASLt | A_cat (3r x Dm bf16) | forward or backward scratch].
+// Forward: X_ext = [x | s x A_cat^T | 0] (M x Kx, Kx = Dm + 3r padded to 64)
+// and W_ext for q, k, v (N_i x Kx: W_i, then B_i in its own r columns, zeros
+// in the others), so each projection with its LoRA term is one GEMM.
+// Backward: dq, dk, dv; dattn; D_ext = [dq | dk | dv | s t | 0] (M x Kd, Kd =
+// Nq + 2 Nkv + 3r padded to 64) and W_dx = [Wq; Wk; Wv; A_cat; 0] (Kd x Dm),
+// so dx is one GEMM; dA_cat (fp32).
 struct BlockWs {
     size_t att_off, att_bytes, lt_off, acat_off;
-    size_t t_off, dattn_off, dq_off, dk_off, dv_off, dx32_off, dacat_off;
+    size_t xext_off, wext_off[3];                         // forward
+    size_t t_off, dattn_off, dq_off, dk_off, dv_off;      // backward
+    size_t dext_off, wdx_off, dacat_off;
     size_t total;
 };
 
 BlockWs block_ws(int is_bwd, const s2block_config* c, const s2attn_opts* att, const Dims& d) {
     BlockWs w{};
     size_t off = 0;
+    const int64_t Nt = d.Nq + 2 * d.Nkv;
+    const int64_t Kx = kpad(d.Dm + 3 * d.r), Kd = kpad(Nt + 3 * d.r);
     w.att_off = off;
     w.att_bytes = s2attn_workspace_size(is_bwd, c->B, c->L, c->Hq, c->Hkv, c->d, c->G, att);
     off += align_up(w.att_bytes);
@@ -197,9 +210,17 @@ BlockWs block_ws(int is_bwd, const s2block_config* c, const s2attn_opts* att, co
     off += align_up(kLtWorkspace);
     w.acat_off = off;
     off += align_up((size_t)3 * d.r * d.Dm * 2);
-    if (is_bwd) {
+    if (!is_bwd) {
+        w.xext_off = off;
+        off += align_up((size_t)d.M * Kx * 2);
+        const int64_t ns[3] = {d.Nq, d.Nkv, d.Nkv};
+        for (int i = 0; i < 3; ++i) {
+            w.wext_off[i] = off;
+            off += align_up((size_t)ns[i] * Kx * 2);
+        }
+    } else {
         w.t_off = off;
-        off += align_up((size_t)d.M * 4 * d.r * 2);
+        off += align_up((size_t)d.M * d.r * 2);
         w.dattn_off = off;
         off += align_up((size_t)d.M * d.Nq * 2);
         w.dq_off = off;
@@ -208,8 +229,10 @@ BlockWs block_ws(int is_bwd, const s2block_config* c, const s2attn_opts* att, co
         off += align_up((size_t)d.M * d.Nkv * 2);
         w.dv_off = off;
         off += align_up((size_t)d.M * d.Nkv * 2);
-        w.dx32_off = off;
-        off += align_up((size_t)d.M * d.Dm * 4);
+        w.dext_off = off;
+        off += align_up((size_t)d.M * Kd * 2);
+        w.wdx_off = off;
+        off += align_up((size_t)Kd * d.Dm * 2);
         w.dacat_off = off;
         off += align_up((size_t)3 * d.r * d.Dm * 4);
     }
@@ -297,32 +320,44 @@ int s2block_fwd(const s2block_config* cfg, const void* x, const s2block_params* 
     TRY(setup(ws, ws_bytes, bw, stream, &g));
     char* base = static_cast<char*>(ws);
     char* acat = base + bw.acat_off;
+    char* xext = base + bw.xext_off;
     const int64_t M = d.M, Dm = d.Dm, Nq = d.Nq, Nkv = d.Nkv, r = d.r, ldu = 4 * r;
+    const int64_t Kx = kpad(Dm + 3 * r);
     const float s = cfg->lora_scale;
     char* u = static_cast<char*>(saved->u);
 
-    // LoRA down-projections of x for q, k, v in one pass over x: u[:, 0:3r] = x A_cat^T.
+    // u[:, 0:3r] = s x A_cat^T (the LoRA down-projections for q, k, v, in one
+    // pass over x), then X_ext = [x | u[:, 0:3r]].
     TRY(concat_a(w, acat, d, stream));
-    TRY(g.run(false, true, M, 3 * r, Dm, 1.f, x, Dm, acat, Dm, 0.f, u, ldu, false));
-    // q, k, v = x W^T + s u B^T
+    TRY(g.run(false, true, M, 3 * r, Dm, s, x, Dm, acat, Dm, 0.f, u, ldu, false));
+    if (s2::launch_copy_cols(x, Dm, xext, Kx, M, Dm, stream) != hipSuccess ||
+        s2::launch_copy_cols(u, ldu, xext + Dm * 2, Kx, M, 3 * r, stream) != hipSuccess ||
+        s2::launch_copy_cols(nullptr, 0, xext + (Dm + 3 * r) * 2, Kx, M, Kx - Dm - 3 * r,
+                             stream) != hipSuccess)
+        return S2ATTN_ERR_HIP;
+    // q, k, v = X_ext W_ext^T: W x^T + B (s A x^T) in one GEMM each
     void* outs[3] = {saved->q, saved->k, saved->v};
     const void* ws3[3] = {w->wq, w->wk, w->wv};
     const void* bs3[3] = {w->bq, w->bk, w->bv};
     const int64_t ns[3] = {Nq, Nkv, Nkv};
     for (int i = 0; i < 3; ++i) {
-        TRY(g.run(false, true, M, ns[i], Dm, 1.f, x, Dm, ws3[i], Dm, 0.f, outs[i], ns[i], false));
-        TRY(g.run(false, true, M, ns[i], r, s, u + i * r * 2, ldu, bs3[i], r, 1.f, outs[i], ns[i],
-                  false));
+        char* wext = base + bw.wext_off[i];
+        if (s2::launch_copy_cols(ws3[i], Dm, wext, Kx, ns[i], Dm, stream) != hipSuccess ||
+            s2::launch_copy_cols(nullptr, 0, wext + Dm * 2, Kx, ns[i], Kx - Dm, stream) != hipSuccess ||
+            s2::launch_copy_cols(bs3[i], r, wext + (Dm + i * r) * 2, Kx, ns[i], r, stream) !=
+                hipSuccess)
+            return S2ATTN_ERR_HIP;
+        TRY(g.run(false, true, M, ns[i], Kx, 1.f, xext, Kx, wext, Kx, 0.f, outs[i], ns[i], false));
     }
     // attention (RoPE-PI inside)
     TRY(s2attn_fwd_ex(saved->q, saved->k, saved->v, saved->attn, saved->lse, cfg->B, cfg->L,
                       cfg->Hq, cfg->Hkv, cfg->d, cfg->G, cfg->shifted_heads, &att,
                       bw.att_bytes ? base + bw.att_off : nullptr, bw.att_bytes, stream));
-    // u[:, 3r:4r] = attn Ao^T; y = attn Wo^T + s u_o Bo^T
-    TRY(g.run(false, true, M, r, Nq, 1.f, saved->attn, Nq, w->ao, Nq, 0.f, u + 3 * r * 2, ldu,
+    // u[:, 3r:4r] = s attn Ao^T; y = attn Wo^T + u_o Bo^T
+    TRY(g.run(false, true, M, r, Nq, s, saved->attn, Nq, w->ao, Nq, 0.f, u + 3 * r * 2, ldu,
               false));
     TRY(g.run(false, true, M, Dm, Nq, 1.f, saved->attn, Nq, w->wo, Nq, 0.f, y, Dm, false));
-    TRY(g.run(false, true, M, Dm, r, s, u + 3 * r * 2, ldu, w->bo, r, 1.f, y, Dm, false));
+    TRY(g.run(false, true, M, Dm, r, 1.f, u + 3 * r * 2, ldu, w->bo, r, 1.f, y, Dm, false));
     return S2ATTN_OK;
 }
 
@@ -345,52 +380,66 @@ int s2block_bwd(const s2block_config* cfg, const void* x, const s2block_params* 
     TRY(setup(ws, ws_bytes, bw, stream, &g));
     char* base = static_cast<char*>(ws);
     char* acat = base + bw.acat_off;
-    char* t = base + bw.t_off;  // [M, 4r]: dq Bq | dk Bk | dv Bv | dy Bo
+    char* t_o = base + bw.t_off;  // dy Bo
     char* dattn = base + bw.dattn_off;
     char* dqkv[3] = {base + bw.dq_off, base + bw.dk_off, base + bw.dv_off};
-    float* dx32 = reinterpret_cast<float*>(base + bw.dx32_off);
+    char* dext = base + bw.dext_off;
+    char* wdx = base + bw.wdx_off;
     float* dacat = reinterpret_cast<float*>(base + bw.dacat_off);
     const int64_t M = d.M, Dm = d.Dm, Nq = d.Nq, Nkv = d.Nkv, r = d.r, ldu = 4 * r;
+    const int64_t Nt = Nq + 2 * Nkv, Kd = kpad(Nt + 3 * r);
     const float s = cfg->lora_scale;
-    const char* u = static_cast<const char*>(saved->u);
+    const char* u = static_cast<const char*>(saved->u);  // s x A^T | s attn Ao^T
 
-    // O projection: t_o = dy Bo; dBo = s dy^T u_o; dAo = s t_o^T attn; dattn = dy Wo + s t_o Ao
-    TRY(g.run(false, false, M, r, Dm, 1.f, dy, Dm, w->bo, r, 0.f, t + 3 * r * 2, ldu, false));
-    TRY(g.run(true, false, Dm, r, M, s, dy, Dm, u + 3 * r * 2, ldu, 0.f, gr->dbo, r, true));
-    TRY(g.run(true, false, r, Nq, M, s, t + 3 * r * 2, ldu, saved->attn, Nq, 0.f, gr->dao, Nq,
-              true));
+    // O projection: t_o = dy Bo; dBo = dy^T u_o; dAo = s t_o^T attn; dattn = dy Wo + s t_o Ao
+    TRY(g.run(false, false, M, r, Dm, 1.f, dy, Dm, w->bo, r, 0.f, t_o, r, false));
+    TRY(g.run(true, false, Dm, r, M, 1.f, dy, Dm, u + 3 * r * 2, ldu, 0.f, gr->dbo, r, true));
+    TRY(g.run(true, false, r, Nq, M, s, t_o, r, saved->attn, Nq, 0.f, gr->dao, Nq, true));
     TRY(g.run(false, false, M, Nq, Dm, 1.f, dy, Dm, w->wo, Nq, 0.f, dattn, Nq, false));
-    TRY(g.run(false, false, M, Nq, r, s, t + 3 * r * 2, ldu, w->ao, Nq, 1.f, dattn, Nq, false));
+    TRY(g.run(false, false, M, Nq, r, s, t_o, r, w->ao, Nq, 1.f, dattn, Nq, false));
     // attention backward: gradients w.r.t. the pre-RoPE q, k and v
     TRY(s2attn_bwd_ex(saved->q, saved->k, saved->v, saved->attn, saved->lse, dattn, dqkv[0],
                       dqkv[1], dqkv[2], cfg->B, cfg->L, cfg->Hq, cfg->Hkv, cfg->d, cfg->G,
                       cfg->shifted_heads, &att, base + bw.att_off, bw.att_bytes, stream));
-    // Q, K, V projections: t_i = d_i B_i; dB_i = s d_i^T u_i
+    // D_ext = [dq | dk | dv | s t_qkv] with t_i = dz_i B_i; dB_i = dz_i^T u_i
     const void* bs3[3] = {w->bq, w->bk, w->bv};
     const void* ws3[3] = {w->wq, w->wk, w->wv};
     float* dbs[3] = {gr->dbq, gr->dbk, gr->dbv};
     const int64_t ns[3] = {Nq, Nkv, Nkv};
+    int64_t col = 0;
     for (int i = 0; i < 3; ++i) {
-        TRY(g.run(false, false, M, r, ns[i], 1.f, dqkv[i], ns[i], bs3[i], r, 0.f, t + i * r * 2,
-                  ldu, false));
-        TRY(g.run(true, false, ns[i], r, M, s, dqkv[i], ns[i], u + i * r * 2, ldu, 0.f, dbs[i], r,
-                  true));
+        if (s2::launch_copy_cols(dqkv[i], ns[i], dext + col * 2, Kd, M, ns[i], stream) !=
+            hipSuccess)
+            return S2ATTN_ERR_HIP;
+        col += ns[i];
+        TRY(g.run(false, false, M, r, ns[i], s, dqkv[i], ns[i], bs3[i], r, 0.f,
+                  dext + (Nt + i * r) * 2, Kd, false));
+        TRY(g.run(true, false, ns[i], r, M, 1.f, dqkv[i], ns[i], u + i * r * 2, ldu, 0.f, dbs[i],
+                  r, true));
     }
-    // dA_cat = s t_qkv^T x, split into dAq, dAk, dAv
-    TRY(concat_a(w, acat, d, stream));
-    TRY(g.run(true, false, 3 * r, Dm, M, s, t, ldu, x, Dm, 0.f, dacat, Dm, true));
+    // dA_cat = (s t_qkv)^T x, split into dAq, dAk, dAv
+    TRY(g.run(true, false, 3 * r, Dm, M, 1.f, dext + Nt * 2, Kd, x, Dm, 0.f, dacat, Dm, true));
     float* das[3] = {gr->daq, gr->dak, gr->dav};
     for (int i = 0; i < 3; ++i)
         if (hipMemcpyAsync(das[i], dacat + (size_t)i * r * Dm, (size_t)r * Dm * 4,
                            hipMemcpyDeviceToDevice, stream) != hipSuccess)
             return S2ATTN_ERR_HIP;
-    // dx = dq Wq + dk Wk + dv Wv + s t_qkv A_cat, accumulated in fp32, stored bf16
-    for (int i = 0; i < 3; ++i)
-        TRY(g.run(false, false, M, Dm, ns[i], 1.f, dqkv[i], ns[i], ws3[i], Dm, i ? 1.f : 0.f, dx32,
-                  Dm, true));
-    TRY(g.run(false, false, M, Dm, 3 * r, s, t, ldu, acat, Dm, 1.f, dx32, Dm, true));
-    if (s2::launch_f32_to_bf16(dx32, gr->dx, (size_t)M * Dm, stream) != hipSuccess)
+    // W_dx = [Wq; Wk; Wv; A_cat]; dx = D_ext W_dx (one GEMM, K = Nq + 2 Nkv + 3r)
+    size_t off = 0;
+    for (int i = 0; i < 3; ++i) {
+        const size_t bytes = (size_t)ns[i] * Dm * 2;
+        if (hipMemcpyAsync(wdx + off, ws3[i], bytes, hipMemcpyDeviceToDevice, stream) != hipSuccess)
+            return S2ATTN_ERR_HIP;
+        off += bytes;
+    }
+    TRY(concat_a(w, wdx + off, d, stream));
+    // zero padding: D_ext's last columns against W_dx's last rows
+    if (s2::launch_copy_cols(nullptr, 0, dext + (Nt + 3 * r) * 2, Kd, M, Kd - Nt - 3 * r,
+                             stream) != hipSuccess ||
+        s2::launch_copy_cols(nullptr, 0, wdx + (Nt + 3 * r) * Dm * 2, Dm, Kd - Nt - 3 * r, Dm,
+                             stream) != hipSuccess)
         return S2ATTN_ERR_HIP;
+    TRY(g.run(false, false, M, Dm, Kd, 1.f, dext, Kd, wdx, Dm, 0.f, gr->dx, Dm, false));
     return S2ATTN_OK;
 }
 

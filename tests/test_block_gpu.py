@@ -99,13 +99,14 @@ def test_block_llama7b_32k():
     ry = OB.sampled_forward_tokens(inp["x"], inp["params"], G, wl.shifted_heads, wl.Hq, wl.Hkv,
                                    wl.d, wl.lora_scale, 0, toks, rope=rope)
     _check("y[sampled tokens]", host(y[0, toks]), ry)
-    # dBo = s dy^T (attn Ao^T), dAo = s (dy Bo)^T attn, in fp32 from the saved tensors
+    # dBo = s dy^T (attn Ao^T), dAo = s (dy Bo)^T attn, in fp32 from the saved
+    # tensors (the saved u holds s attn Ao^T)
     s, r = wl.lora_scale, wl.lora_rank
     M = wl.B * wl.L
     dyf = dy.reshape(M, -1).float()
     attn = saved["attn"].reshape(M, -1).float()
     u_o = saved["u"][:, 3 * r:4 * r].float()
-    ref_dbo = s * (dyf.t() @ u_o)
+    ref_dbo = dyf.t() @ u_o
     ref_dao = s * ((dyf @ params["bo"].float()).t() @ attn)
     _check("dbo (vs fp32 product)", host(g["dbo"]), host(ref_dbo))
     _check("dao (vs fp32 product)", host(g["dao"]), host(ref_dao))
