@@ -120,6 +120,16 @@ int s2attn_bwd(const void* q, const void* k, const void* v, const void* o,
  * Bytes of workspace the _ex entry points need for these sizes and options
  * (0 when none).  is_bwd selects the backward.  Returns 0 for invalid
  * arguments as well; the _ex call then reports the error.
+ *
+ * Backward workspace, each part 256-byte aligned: delta and lse * log2(e)
+ * (2 B Hq L floats); with RoPE the rotated q and k (bf16, the sizes of q and
+ * k); for bf16 inputs, the dS tiles: per (batch, head, group) the 32 x 32
+ * tiles on or below the causal diagonal, T (T + 1) / 2 tiles of 2 KB with
+ * T = ceil(G / 32), i.e. B Hq (L / G) T (T + 1) / 2 * 2048 bytes (about
+ * B Hq L G bytes), kept only while that is at most 32 GiB.  The dK/dV kernel
+ * writes dS there and the dQ kernel reads it, so dQ is one product instead
+ * of recomputing the scores; above the bound dQ recomputes them.  The plain
+ * s2attn_bwd has no workspace and always recomputes.
  */
 size_t s2attn_workspace_size(int is_bwd, int B, int L, int Hq, int Hkv, int d, int G,
                              const s2attn_opts* opts);
@@ -140,11 +150,14 @@ int s2attn_bwd_ex(const void* q, const void* k, const void* v, const void* o,
  * Arguments are those of s2attn_bwd_ex, with the same workspace.
  *   S2ATTN_BWD_STAGE_PRE   delta = rowsum(dout * o) into the workspace (and,
  *                          with RoPE, the rotated q and k).
- *   S2ATTN_BWD_STAGE_DKDV  dk, dv.  Needs PRE complete.
- *   S2ATTN_BWD_STAGE_DQ    dq.  Needs PRE complete.
- * PRE, DKDV, DQ in that order on one stream equal s2attn_bwd_ex; DKDV and DQ
- * read only PRE's results and the inputs, so they may run concurrently on two
- * streams once PRE has finished.  Any other stage value: S2ATTN_ERR_INVALID_ARG.
+ *   S2ATTN_BWD_STAGE_DKDV  dk, dv (and, bf16, the dS tiles into the
+ *                          workspace when it holds them).  Needs PRE complete.
+ *   S2ATTN_BWD_STAGE_DQ    dq.  Needs PRE complete, and DKDV complete when the
+ *                          workspace holds dS tiles (see s2attn_workspace_size).
+ * PRE, DKDV, DQ in that order on one stream equal s2attn_bwd_ex.  Without dS
+ * tiles (fp32, or groups too large) DKDV and DQ read only PRE's results and
+ * the inputs and may run concurrently on two streams once PRE has finished.
+ * Any other stage value: S2ATTN_ERR_INVALID_ARG.
  */
 int s2attn_bwd_stage_ex(int stage, const void* q, const void* k, const void* v, const void* o,
                         const float* lse, const void* dout, void* dq, void* dk, void* dv,

@@ -133,6 +133,14 @@ __device__ __forceinline__ void wait_vmem() {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt/lgkmcnt untouched
 }
 
+// Wait until at most N vector memory operations of this wave are in flight.
+// They complete in issue order, so this awaits all but the last N issued.
+template <int N>
+__device__ __forceinline__ void wait_vmem_n() {
+    static_assert(N >= 0 && N < 16, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
 // One 1 KB chunk `cc` of a row-major swizzled tile with D bf16 columns: the
 // tile row and the byte offset of the logical 16-byte column slot that lane
 // `lane` must fetch so that the DMA lands it at its swizzled place (the XOR

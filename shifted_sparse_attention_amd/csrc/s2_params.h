@@ -22,6 +22,15 @@ struct Params {
     void* dv;
     float* delta;   // [B, Hq, L] rowsum(dout * o), then [B, Hq, L] lse * log2(e)
     float* lse2;
+    // dS tiles of the backward (null: dQ recomputes S and dP).  For unit
+    // (b, h, g), tile (q32, k32) with k32 <= q32 < ceil(G/32) holds dS of
+    // queries 32 q32 .. +31 against keys 32 k32 .. +31, 2 KB at byte
+    // (unit * T (T + 1) / 2 + q32 (q32 + 1) / 2 + k32) * 2048 with
+    // T = ceil(G / 32) and unit = (b Hq + h) n_g + g.  Within a tile, the
+    // four bf16 of key r (0..31) and query quad c (queries 4c .. 4c+3) sit at
+    // byte 1024 (c >> 2) + 16 (r + 32 (c & 1)) + 8 ((c >> 1) & 1): the order
+    // the dK/dV kernel holds them in registers.
+    void* ds;
     // Sizes.
     int B, L, Hq, Hkv, d, G, shifted_heads;
     int r;          // Hq / Hkv
@@ -57,6 +66,7 @@ hipError_t launch_fwd_f32(const Params& p, hipStream_t s);
 hipError_t launch_bwd_pre(const Params& p, int f32_io, hipStream_t s);
 hipError_t launch_bwd_dkdv_bf16(const Params& p, int grad_f32, hipStream_t s);
 hipError_t launch_bwd_dq_bf16(const Params& p, int grad_f32, hipStream_t s);
+hipError_t launch_bwd_dq_ds_bf16(const Params& p, int grad_f32, hipStream_t s);
 hipError_t launch_bwd_dkdv_f32(const Params& p, hipStream_t s);
 hipError_t launch_bwd_dq_f32(const Params& p, hipStream_t s);
 hipError_t launch_rope_prepass(const Params& p, void* q_out, void* k_out, hipStream_t s);

@@ -72,19 +72,36 @@ int resolve_opts(const s2attn_opts* o, int d, Resolved* r) {
 
 size_t elem_size(int dtype) { return dtype == S2ATTN_F32 ? 4 : 2; }
 
-// Workspace layout: [row terms (bwd): delta and lse*log2(e) | rotated q | rotated k],
-// each 256-byte aligned.
+// The backward keeps dS (bf16, 32 x 32 tiles of each group's causal
+// triangle) for the dQ kernel when it fits this bound; above it, dQ
+// recomputes S and dP instead.
+constexpr double kMaxDsBytes = 32.0 * (1ull << 30);
+
+size_t ds_bytes(int B, int Hq, int L, int G) {
+    const size_t T = ((size_t)G + 31) / 32;
+    return (size_t)B * Hq * (L / G) * (T * (T + 1) / 2) * 2048;
+}
+
+bool use_ds(int B, int Hq, int L, int G, const Resolved& r) {
+    return r.dtype == S2ATTN_BF16 && (double)ds_bytes(B, Hq, L, G) <= kMaxDsBytes;
+}
+
+// Workspace layout: [row terms (bwd): delta and lse*log2(e) | rotated q | rotated k |
+// dS tiles (bwd, when kept)], each 256-byte aligned.
 struct WsLayout {
     size_t delta_off, delta_bytes;
     size_t rq_off, rq_bytes;
     size_t rk_off, rk_bytes;
+    size_t ds_off, ds_bytes;
     size_t total;
 };
 
-WsLayout ws_layout(int is_bwd, int B, int L, int Hq, int Hkv, int d, const Resolved& r) {
+// is_bwd: 0 forward, 1 backward with the row terms in the workspace, 2 backward
+// with the row terms supplied separately (the plain entry point: no dS tiles).
+WsLayout ws_layout(int is_bwd, int B, int L, int Hq, int Hkv, int d, int G, const Resolved& r) {
     WsLayout w{};
     size_t off = 0;
-    if (is_bwd) {
+    if (is_bwd == 1) {
         w.delta_off = off;
         w.delta_bytes = 2 * (size_t)B * Hq * L * sizeof(float);
         off += align_up(w.delta_bytes);
@@ -96,6 +113,11 @@ WsLayout ws_layout(int is_bwd, int B, int L, int Hq, int Hkv, int d, const Resol
         w.rk_off = off;
         w.rk_bytes = (size_t)B * L * Hkv * d * 2;
         off += align_up(w.rk_bytes);
+    }
+    if (is_bwd == 1 && use_ds(B, Hq, L, G, r)) {
+        w.ds_off = off;
+        w.ds_bytes = ds_bytes(B, Hq, L, G);
+        off += align_up(w.ds_bytes);
     }
     w.total = off;
     return w;
@@ -140,7 +162,7 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
     Resolved r;
     st = resolve_opts(opts, d, &r);
     if (st) return st;
-    const WsLayout wl = ws_layout(0, B, L, Hq, Hkv, d, r);
+    const WsLayout wl = ws_layout(0, B, L, Hq, Hkv, d, G, r);
     if (wl.total > 0 && (ws == nullptr || ws_bytes < wl.total || !aligned16(ws)))
         return S2ATTN_ERR_WORKSPACE;
 
@@ -181,12 +203,12 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const f
     if (st) return st;
     if (shifted_heads % (Hq / Hkv) != 0) return S2ATTN_ERR_UNSUPPORTED;
 
-    WsLayout wl = ws_layout(1, B, L, Hq, Hkv, d, r);
+    WsLayout wl = ws_layout(1, B, L, Hq, Hkv, d, G, r);
     char* base = static_cast<char*>(ws);
     if (delta != nullptr) {
         // Plain entry point: delta supplied separately, workspace holds the rest.
         if (!aligned16(delta)) return S2ATTN_ERR_INVALID_ARG;
-        wl = ws_layout(0, B, L, Hq, Hkv, d, r);
+        wl = ws_layout(2, B, L, Hq, Hkv, d, G, r);
     }
     if (wl.total > 0 && (ws == nullptr || ws_bytes < wl.total || !aligned16(ws)))
         return S2ATTN_ERR_WORKSPACE;
@@ -204,6 +226,7 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const f
     p.dv = dv;
     p.delta = delta;
     p.lse2 = delta + (size_t)B * Hq * L;
+    p.ds = wl.ds_bytes ? base + wl.ds_off : nullptr;
 
     char* rq = base + wl.rq_off;
     char* rk = base + wl.rk_off;
@@ -225,7 +248,8 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const f
     }
     if (stages & kStageDq) {
         hipError_t e = r.dtype == S2ATTN_F32 ? s2::launch_bwd_dq_f32(p, stream)
-                                              : s2::launch_bwd_dq_bf16(p, gf, stream);
+                       : p.ds               ? s2::launch_bwd_dq_ds_bf16(p, gf, stream)
+                                            : s2::launch_bwd_dq_bf16(p, gf, stream);
         if (e != hipSuccess) return S2ATTN_ERR_HIP;
     }
     return S2ATTN_OK;
@@ -281,7 +305,7 @@ size_t s2attn_workspace_size(int is_bwd, int B, int L, int Hq, int Hkv, int d, i
     if (check_sizes(B, L, Hq, Hkv, d, G, 0) != S2ATTN_OK) return 0;
     Resolved r;
     if (resolve_opts(opts, d, &r) != S2ATTN_OK) return 0;
-    return ws_layout(is_bwd ? 1 : 0, B, L, Hq, Hkv, d, r).total;
+    return ws_layout(is_bwd ? 1 : 0, B, L, Hq, Hkv, d, G, r).total;
 }
 
 int s2attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int L,

@@ -320,10 +320,18 @@ __global__ __launch_bounds__(64 * DKV_WAVES) void bwd_dkdv_bf16_kernel(Params p,
         dv[cb] = f32x16{};
     }
 
+    // dS stores of the previous step still in flight (0 or 2; wave-uniform):
+    // they were issued after that step's loads, so waiting down to them awaits
+    // the loads and leaves the stores a whole step to drain.
+    int ds_inflight = 0;
     for (int it = 0; it < n_it; ++it) {
-        wait_vmem();
+        if (ds_inflight)
+            wait_vmem_n<2>();
+        else
+            wait_vmem();
         __syncthreads();
         if (it + 1 < n_it) stage(it + 1, (it + 1) & 1);
+        ds_inflight = 0;
         const int qb = (qt_first + it % nq) * DKV_BQ + 32 * qh;  // first query of this wave
         if (qb + 31 < kw) continue;  // every query of the half-tile is before every key
         const bool masked = (qb < kw + 31) || (qb + 32 > p.G);
@@ -375,6 +383,20 @@ __global__ __launch_bounds__(64 * DKV_WAVES) void bwd_dkdv_bf16_kernel(Params p,
             }
             pb[kk] = to_bf16x8(t1);
             db[kk] = to_bf16x8(t2);
+        }
+        if (p.ds != nullptr && qb < p.G) {
+            // dS tile out for the dQ kernel, in register order: db[kk] of
+            // every lane at byte 1024 kk + 16 lane, so each store writes 1 KB
+            // of whole cache lines.  Streaming (non-temporal): it is read once.
+            const size_t T = (p.G + 31) / 32;
+            const int q32 = qb >> 5, k32 = kw >> 5;
+            const int h = hk * p.r + it / nq;
+            const size_t tile = (((size_t)w.b * p.Hq + h) * p.n_g + w.g) * (T * (T + 1) / 2) +
+                                (size_t)q32 * (q32 + 1) / 2 + k32;
+            u32x4* out = reinterpret_cast<u32x4*>(static_cast<char*>(p.ds) + tile * 2048) + lane;
+            __builtin_nontemporal_store(__builtin_bit_cast(u32x4, db[0]), out);
+            __builtin_nontemporal_store(__builtin_bit_cast(u32x4, db[1]), out + 64);
+            ds_inflight = 2;
         }
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
@@ -546,6 +568,149 @@ __global__ __launch_bounds__(64 * DQ_WAVES) void bwd_dq_bf16_kernel(Params p, in
         return;
     }
     __syncthreads();  // every wave is done with the K/V buffers
+    char* st = smem + wave * 32 * D * 2;
+    stage_rows_bf16<D>(dq, st, lane);
+    __syncthreads();
+    flush_rows<D>(p, st, p.dq, w.b, p.Hq, w.h, w.g, s, qw, lane);
+}
+
+// ---------------------------------------------------------------------------
+// bf16 dQ from stored dS.  When the dK/dV kernel has written its dS tiles
+// (dS^T per 32 keys x 32 queries, see Params::ds), dQ = scale dS K needs no
+// recomputation of S and dP: one product instead of three.  8 waves x 32
+// queries per workgroup; K tiles of 64 keys and each wave's two dS^T tiles
+// stream through three LDS buffers by direct global->LDS loads, two stages in
+// flight while one is consumed (the loop is bound by load latency, not MFMA).
+//   dQ^T += K^T dS^T   (A: transposed reads of the K tile; B: transposed
+//                        reads of the dS^T tiles, in the same key order)
+// ---------------------------------------------------------------------------
+constexpr int DQS_WAVES = 8;
+constexpr int DQS_BQ = 32 * DQS_WAVES;
+constexpr int DQS_BK = 64;
+constexpr int DQS_NBUF = 3;  // stages in LDS: two in flight while one is consumed
+
+// Wait until at most n (wave-uniform, 0..7) vector memory operations are in flight.
+__device__ __forceinline__ void wait_vmem_upto(int n) {
+    switch (n) {
+        case 0: wait_vmem_n<0>(); break;
+        case 1: wait_vmem_n<1>(); break;
+        case 2: wait_vmem_n<2>(); break;
+        case 3: wait_vmem_n<3>(); break;
+        case 4: wait_vmem_n<4>(); break;
+        case 5: wait_vmem_n<5>(); break;
+        case 6: wait_vmem_n<6>(); break;
+        default: wait_vmem_n<7>(); break;
+    }
+}
+
+template <int D, bool GRAD_F32>
+__global__ __launch_bounds__(64 * DQS_WAVES) void bwd_dq_ds_kernel(Params p, int n_qt) {
+    constexpr int CB = D / 32;
+    constexpr int KTILE = DQS_BK * D * 2;      // one K tile
+    constexpr int KNCH = KTILE / 1024;
+    constexpr int DSW = 2 * 2048;              // a wave's two dS^T tiles
+    constexpr int STAGE = KTILE + DQS_WAVES * DSW;
+    static_assert(KNCH % DQS_WAVES == 0, "K chunks per wave");
+    __shared__ __attribute__((aligned(1024))) char smem[DQS_NBUF * STAGE];
+
+    const int n_units = p.B * p.Hq * p.n_g;
+    const Work w = decode_work(blockIdx.x, n_units, n_qt, p.Hq, p.n_g);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int hh = lane >> 5;
+    const int g16 = lane >> 4, jj = lane & 15;
+    const int s = head_shift(p, w.h);
+    const int hk = w.h / p.r;
+    const bf16* __restrict__ k = static_cast<const bf16*>(p.k);
+
+    const int q0 = w.tile * DQS_BQ;
+    const int qw = q0 + wave * 32;
+    const int q32 = qw >> 5;
+    const bool wave_valid = qw < p.G;   // the wave owns queries of the group
+    const int q_end = min(q0 + DQS_BQ, p.G);
+    const int n_kt = (q_end + DQS_BK - 1) / DQS_BK;
+    const size_t T = (p.G + 31) / 32;
+    const char* ds_unit = static_cast<const char*>(p.ds) +
+                          (((size_t)w.b * p.Hq + w.h) * p.n_g + w.g) * (T * (T + 1) / 2) * 2048;
+
+    const uint32_t rowb = (uint32_t)p.Hkv * D * 2;
+    const size_t plane = ((size_t)w.b * p.L * p.Hkv + hk) * D;
+    // Loads this wave issues for stage kt (uniform across the wave).
+    auto n_loads = [&](int kt) {
+        return KNCH / DQS_WAVES + (wave_valid ? 2 * ((2 * kt <= q32) + (2 * kt + 1 <= q32)) : 0);
+    };
+    // K tile kt and this wave's dS^T tiles (key tiles 2kt, 2kt + 1 when they
+    // are at or before its queries) -> buffer `buf`.
+    auto stage = [&](int kt, int buf) {
+        char* base = smem + buf * STAGE;
+#pragma unroll
+        for (int j = 0; j < KNCH / DQS_WAVES; ++j) {
+            const int cc = wave + DQS_WAVES * j;
+            const ChunkSlot sl = chunk_slot<D>(cc, lane);
+            const uint32_t off = row_off(w.g, p.G, kt * DQS_BK + sl.row, s, p.L, rowb) + sl.colb;
+            dma16(k + plane, off, base + cc * 1024);
+        }
+        if (wave_valid) {
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb) {
+                const int k32 = 2 * kt + sb;
+                if (k32 <= q32) {
+                    const char* tile = ds_unit + ((size_t)q32 * (q32 + 1) / 2 + k32) * 2048;
+                    char* dst = base + KTILE + wave * DSW + sb * 2048;
+                    dma16(tile, 16u * lane, dst);
+                    dma16(tile + 1024, 16u * lane, dst + 1024);
+                }
+            }
+        }
+    };
+    stage(0, 0);
+    if (n_kt > 1) stage(1, 1);
+
+    f32x16 dq[CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) dq[cb] = f32x16{};
+
+    int buf = 0;  // kt % DQS_NBUF
+    for (int kt = 0; kt < n_kt; ++kt) {
+        // Stage kt landed (stage kt + 1, issued after it, may still be in
+        // flight); after the barrier every wave has also finished reading the
+        // buffer that stage kt + 2 overwrites (consumed at step kt - 1).
+        wait_vmem_upto(kt + 1 < n_kt ? n_loads(kt + 1) : 0);
+        __syncthreads();
+        if (kt + 2 < n_kt) stage(kt + 2, buf == 0 ? 2 : buf - 1);
+        const char* sK = smem + buf * STAGE;
+        buf = buf == DQS_NBUF - 1 ? 0 : buf + 1;
+        if (!wave_valid || 2 * kt > q32) continue;
+        const int n_kk = 2 * kt + 1 <= q32 ? 4 : 2;  // 16-key steps with stored dS
+        const char* sD = sK + KTILE + wave * DSW;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            if (kk >= n_kk) break;
+            // B: dS^T rows (keys) 16kk + 4hh + {0..3, 8..11}, column = this
+            // lane's query (see Params::ds for where key r, quad c sits).
+            const int drow = 16 * (kk & 1) + 4 * hh + (jj >> 2);
+            const int quad = 4 * (g16 & 1) + (jj & 3);
+            const int dbyte = (quad >> 2) * 1024 + 512 * (quad & 1) + 8 * ((quad >> 1) & 1);
+            const char* dsb = sD + (kk >> 1) * 2048;
+            const bf16x8 dsv = cat(ld_lds_tr(dsb, drow * 16 + dbyte),
+                                   ld_lds_tr(dsb, (drow + 8) * 16 + dbyte));
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) {
+                const int col = 32 * cb + 16 * (g16 & 1) + 4 * (jj & 3);
+                const int row = 16 * kk + 4 * hh + (jj >> 2);
+                const bf16x8 kt_ = cat(ld_lds_tr(sK, tile_off<D>(row, col)),
+                                       ld_lds_tr(sK, tile_off<D>(row + 8, col)));
+                dq[cb] = mfma32(kt_, dsv, dq[cb]);
+            }
+        }
+    }
+
+    grad_rows<D>(p, dq, p.scale, w.g, s, qw, lane, p.rope != 0);
+    if (GRAD_F32) {
+        store_rows_f32<D>(p, dq, p.dq, w.b, p.Hq, w.h, w.g, s, qw, lane);
+        return;
+    }
+    __syncthreads();  // every wave is done with the buffers
     char* st = smem + wave * 32 * D * 2;
     stage_rows_bf16<D>(dq, st, lane);
     __syncthreads();
@@ -756,6 +921,22 @@ hipError_t launch_bwd_dkdv_bf16(const Params& p, int grad_f32, hipStream_t st) {
         grad_f32 ? launch_dkdv_t<128, true>(p, st) : launch_dkdv_t<128, false>(p, st);
     else
         grad_f32 ? launch_dkdv_t<64, true>(p, st) : launch_dkdv_t<64, false>(p, st);
+    return hipGetLastError();
+}
+
+template <int D, bool GF>
+static void launch_dq_ds_t(const Params& p, hipStream_t st) {
+    const int n_qt = (p.G + DQS_BQ - 1) / DQS_BQ;
+    const long blocks = (long)p.B * p.Hq * p.n_g * n_qt;
+    hipLaunchKernelGGL((bwd_dq_ds_kernel<D, GF>), dim3(blocks), dim3(64 * DQS_WAVES), 0, st, p,
+                       n_qt);
+}
+
+hipError_t launch_bwd_dq_ds_bf16(const Params& p, int grad_f32, hipStream_t st) {
+    if (p.d == 128)
+        grad_f32 ? launch_dq_ds_t<128, true>(p, st) : launch_dq_ds_t<128, false>(p, st);
+    else
+        grad_f32 ? launch_dq_ds_t<64, true>(p, st) : launch_dq_ds_t<64, false>(p, st);
     return hipGetLastError();
 }
 

@@ -151,13 +151,23 @@ def test_workspace_sizes_and_checks():
     o = s2.s2attn_opts_init()
     B, Ln, Hq, Hkv, d, G = 1, 256, 4, 2, 64, 64
     assert s2.s2attn_workspace_size(0, B, Ln, Hq, Hkv, d, G, o) == 0
+    r256 = lambda x: (x + 255) // 256 * 256
     delta = 2 * B * Hq * Ln * 4     # delta and lse * log2(e)
-    assert s2.s2attn_workspace_size(1, B, Ln, Hq, Hkv, d, G, o) == (delta + 255) // 256 * 256
+    # dS tiles: per (batch, head, group) the 32 x 32 bf16 tiles of the causal triangle
+    T = (G + 31) // 32
+    ds = B * Hq * (Ln // G) * (T * (T + 1) // 2) * 2048
+    assert s2.s2attn_workspace_size(1, B, Ln, Hq, Hkv, d, G, o) == r256(delta) + r256(ds)
+    o.dtype = o.grad_dtype = s2.S2ATTN_F32   # fp32 backward recomputes dS: no tiles
+    assert s2.s2attn_workspace_size(1, B, Ln, Hq, Hkv, d, G, o) == r256(delta)
+    o.dtype = o.grad_dtype = s2.S2ATTN_BF16
+    Gr = 80                          # ragged last tile row (T = 3)
+    dsr = B * Hq * (240 // Gr) * 6 * 2048
+    assert s2.s2attn_workspace_size(1, B, 240, Hq, Hkv, d, Gr, o) == r256(2 * B * Hq * 240 * 4) + r256(dsr)
     o.rope = 1
     rq, rk = B * Ln * Hq * d * 2, B * Ln * Hkv * d * 2
-    r256 = lambda x: (x + 255) // 256 * 256
     assert s2.s2attn_workspace_size(0, B, Ln, Hq, Hkv, d, G, o) == r256(rq) + r256(rk)
-    assert s2.s2attn_workspace_size(1, B, Ln, Hq, Hkv, d, G, o) == r256(delta) + r256(rq) + r256(rk)
+    assert s2.s2attn_workspace_size(1, B, Ln, Hq, Hkv, d, G, o) == (
+        r256(delta) + r256(rq) + r256(rk) + r256(ds))
     assert s2.s2attn_workspace_size(0, 0, Ln, Hq, Hkv, d, G, o) == 0   # invalid sizes -> 0
     # missing / short workspace
     need = s2.s2attn_workspace_size(0, B, Ln, Hq, Hkv, d, G, o)

@@ -382,3 +382,38 @@ def test_every_output_written_and_no_stray_writes():
     rdq, rdk, rdv, ro, rl = O.backward(q, k, v, do, G, sh)
     check("o", host(o.view(B, L, Hq, d)), ro, BF16_REL_F, BF16_MAX_ABS)
     check("dk", host(dk.view(B, L, Hkv, d)), rdk, BF16_REL_F, BF16_MAX_ABS)
+
+
+@pytest.mark.parametrize("rope", [None, (10000.0, 64)])
+def test_workspace_writes_stay_inside(rope):
+    """The _ex backward writes only inside its workspace (delta, rotated q/k,
+    the dS tiles of a ragged group: G = 200 leaves an 8-query last tile),
+    and the stored-dS dQ path agrees with the recomputing one of s2attn_bwd."""
+    B, L, Hq, Hkv, d, G, sh = 1, 600, 4, 2, 128, 200, 2
+    say(f"[invariant] workspace redzones rope={rope}")
+    q, k, v, do = rand_inputs(31, B, L, Hq, Hkv, d)
+    tq, tk, tv, tdo = (dev(x, BF) for x in (q, k, v, do))
+    o, lse = s2.forward(tq, tk, tv, G, sh, rope=rope)
+    opts = s2.make_opts(BF, rope=rope)
+    n = s2.s2attn_workspace_size(1, B, L, Hq, Hkv, d, G, opts)
+    T = (G + 31) // 32
+    assert n >= B * Hq * (L // G) * T * (T + 1) // 2 * 2048
+    pad = 1 << 16
+    SENT = 0x5A
+    buf = torch.full((n + 2 * pad,), SENT, dtype=torch.uint8, device="cuda")
+    ws = buf[pad:pad + n]
+    dq, dk, dv = (torch.empty_like(x) for x in (tq, tk, tv))
+    s2.s2attn_bwd_ex(tq, tk, tv, o, lse, tdo, dq, dk, dv, B, L, Hq, Hkv, d, G, sh, opts, ws, n)
+    torch.cuda.synchronize()
+    assert (buf[:pad] == SENT).all() and (buf[-pad:] == SENT).all()
+    rdq, rdk, rdv, _, _ = O.backward(q, k, v, do, G, sh, rope=rope)
+    for name, a, ref in (("dq", dq, rdq), ("dk", dk, rdk), ("dv", dv, rdv)):
+        check(name, host(a), ref, BF16_REL_F, bf16_store_tol(ref))
+    if rope is None:
+        pq = torch.empty_like(tq)
+        pk, pv = torch.empty_like(tk), torch.empty_like(tv)
+        de = torch.empty(2 * B * Hq * L, dtype=torch.float32, device="cuda")
+        s2.s2attn_bwd(tq, tk, tv, o, lse, tdo, pq, pk, pv, de, B, L, Hq, Hkv, d, G, sh)
+        torch.cuda.synchronize()
+        check("dq (recompute path)", host(pq), rdq, BF16_REL_F, bf16_store_tol(rdq))
+        assert torch.equal(pk, dk) and torch.equal(pv, dv)   # same dK/dV kernel
