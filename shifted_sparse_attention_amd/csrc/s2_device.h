@@ -135,10 +135,11 @@ __device__ __forceinline__ void wait_vmem() {
 
 // Wait until at most N vector memory operations of this wave are in flight.
 // They complete in issue order, so this awaits all but the last N issued.
+// (vmcnt is 6 bits: 3:0 and 15:14 of the immediate.)
 template <int N>
 __device__ __forceinline__ void wait_vmem_n() {
-    static_assert(N >= 0 && N < 16, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
 // One 1 KB chunk `cc` of a row-major swizzled tile with D bf16 columns: the

@@ -286,17 +286,17 @@ __global__ __launch_bounds__(64 * DKV_WAVES) void bwd_dkdv_bf16_kernel(Params p,
             dma16((isv ? v : k) + plane, off, (isv ? sVt : sKt) + cc * 1024);
         }
     }
-    // Q, dO, lse2, delta of step `it` (query head hk*r + it/nq, tile qt_first + it%nq).
-    // Rows past the group are clamped to its last row and masked in the loop.
+    // Q, dO, lse2, delta of a step: query head h, tile qt_first + t.  Steps
+    // walk t = 0 .. nq - 1 for each query head of the KV head in turn.  Rows
+    // past the group are clamped to its last row and masked in the loop.
     constexpr int NSLOT = 2 * NCH / DKV_WAVES;  // 1 KB chunks per wave per tile; Q first, then dO
     const uint32_t qrowb = (uint32_t)p.Hq * D * 2;
     ChunkSlot slot[NSLOT];
 #pragma unroll
     for (int j = 0; j < NSLOT; ++j) slot[j] = chunk_slot<D>((wave + DKV_WAVES * j) % NCH, lane);
-    auto stage = [&](int it, int buf) {
+    auto stage = [&](int h, int t, int buf) {
         char* base = bufs + buf * BUF;
-        const int h = hk * p.r + it / nq;
-        const int q0 = (qt_first + it % nq) * DKV_BQ;
+        const int q0 = (qt_first + t) * DKV_BQ;
         const size_t plane = ((size_t)w.b * p.L * p.Hq + h) * D;
 #pragma unroll
         for (int j = 0; j < NSLOT; ++j) {
@@ -311,7 +311,7 @@ __global__ __launch_bounds__(64 * DKV_WAVES) void bwd_dkdv_bf16_kernel(Params p,
             dma4(rb, off, base + 2 * TILE + wave * DKV_BQ * 4);
         }
     };
-    stage(0, 0);
+    stage(hk * p.r, 0, 0);
 
     f32x16 dk[CB], dv[CB];
 #pragma unroll
@@ -320,6 +320,17 @@ __global__ __launch_bounds__(64 * DKV_WAVES) void bwd_dkdv_bf16_kernel(Params p,
         dv[cb] = f32x16{};
     }
 
+    // dS tiles of the current query head (see Params::ds): the head's base
+    // and the tile of this wave's keys in query row q32 at
+    // + (q32 (q32 + 1) / 2 + kw / 32) * 2048.
+    const size_t TT = ((size_t)(p.G + 31) / 32) * ((p.G + 31) / 32 + 1) / 2;
+    auto ds_head = [&](int h) {
+        return p.ds == nullptr ? nullptr
+                               : static_cast<char*>(p.ds) +
+                                     (((size_t)w.b * p.Hq + h) * p.n_g + w.g) * TT * 2048;
+    };
+    int h = hk * p.r, t = 0;   // current step
+    char* ds_base = ds_head(h);
     // dS stores of the previous step still in flight (0 or 2; wave-uniform):
     // they were issued after that step's loads, so waiting down to them awaits
     // the loads and leaves the stores a whole step to drain.
@@ -330,9 +341,20 @@ __global__ __launch_bounds__(64 * DKV_WAVES) void bwd_dkdv_bf16_kernel(Params p,
         else
             wait_vmem();
         __syncthreads();
-        if (it + 1 < n_it) stage(it + 1, (it + 1) & 1);
+        if (it + 1 < n_it) {
+            if (t + 1 < nq)
+                stage(h, t + 1, (it + 1) & 1);
+            else
+                stage(h + 1, 0, (it + 1) & 1);
+        }
         ds_inflight = 0;
-        const int qb = (qt_first + it % nq) * DKV_BQ + 32 * qh;  // first query of this wave
+        const int qb = (qt_first + t) * DKV_BQ + 32 * qh;  // first query of this wave
+        char* const it_ds = ds_base;
+        if (++t == nq) {
+            t = 0;
+            ++h;
+            ds_base = ds_head(h);
+        }
         if (qb + 31 < kw) continue;  // every query of the half-tile is before every key
         const bool masked = (qb < kw + 31) || (qb + 32 > p.G);
         const char* sQ = bufs + (it & 1) * BUF + 32 * qh * D * 2;
@@ -384,16 +406,13 @@ __global__ __launch_bounds__(64 * DKV_WAVES) void bwd_dkdv_bf16_kernel(Params p,
             pb[kk] = to_bf16x8(t1);
             db[kk] = to_bf16x8(t2);
         }
-        if (p.ds != nullptr && qb < p.G) {
+        if (it_ds != nullptr && qb < p.G) {
             // dS tile out for the dQ kernel, in register order: db[kk] of
             // every lane at byte 1024 kk + 16 lane, so each store writes 1 KB
             // of whole cache lines.  Streaming (non-temporal): it is read once.
-            const size_t T = (p.G + 31) / 32;
-            const int q32 = qb >> 5, k32 = kw >> 5;
-            const int h = hk * p.r + it / nq;
-            const size_t tile = (((size_t)w.b * p.Hq + h) * p.n_g + w.g) * (T * (T + 1) / 2) +
-                                (size_t)q32 * (q32 + 1) / 2 + k32;
-            u32x4* out = reinterpret_cast<u32x4*>(static_cast<char*>(p.ds) + tile * 2048) + lane;
+            const uint32_t q32 = qb >> 5, k32 = kw >> 5;
+            const size_t tile = (size_t)q32 * (q32 + 1) / 2 + k32;
+            u32x4* out = reinterpret_cast<u32x4*>(it_ds + tile * 2048) + lane;
             __builtin_nontemporal_store(__builtin_bit_cast(u32x4, db[0]), out);
             __builtin_nontemporal_store(__builtin_bit_cast(u32x4, db[1]), out + 64);
             ds_inflight = 2;
@@ -421,6 +440,20 @@ __global__ __launch_bounds__(64 * DKV_WAVES) void bwd_dkdv_bf16_kernel(Params p,
     reduce_store<D, GRAD_F32>(p, dk, red, stg, p.scale, p.rope != 0, p.dk, w.b, hk, w.g, s, kw,
                               lane, qh);
     reduce_store<D, GRAD_F32>(p, dv, red, stg, 1.0f, false, p.dv, w.b, hk, w.g, s, kw, lane, qh);
+}
+
+// Wait until at most n (wave-uniform) vector memory operations are in flight;
+// n above 15 waits down to 15, which is only stricter.
+__device__ __forceinline__ void wait_vmem_upto(int n) {
+    switch (n) {
+#define S2_WAIT_CASE(N) \
+    case N: wait_vmem_n<N>(); break;
+        S2_WAIT_CASE(0) S2_WAIT_CASE(1) S2_WAIT_CASE(2) S2_WAIT_CASE(3) S2_WAIT_CASE(4)
+        S2_WAIT_CASE(5) S2_WAIT_CASE(6) S2_WAIT_CASE(7) S2_WAIT_CASE(8) S2_WAIT_CASE(9)
+        S2_WAIT_CASE(10) S2_WAIT_CASE(11) S2_WAIT_CASE(12) S2_WAIT_CASE(13) S2_WAIT_CASE(14)
+#undef S2_WAIT_CASE
+        default: wait_vmem_n<15>(); break;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -578,40 +611,33 @@ __global__ __launch_bounds__(64 * DQ_WAVES) void bwd_dq_bf16_kernel(Params p, in
 // bf16 dQ from stored dS.  When the dK/dV kernel has written its dS tiles
 // (dS^T per 32 keys x 32 queries, see Params::ds), dQ = scale dS K needs no
 // recomputation of S and dP: one product instead of three.  8 waves x 32
-// queries per workgroup; K tiles of 64 keys and each wave's two dS^T tiles
+// queries per workgroup; K tiles of 64 keys and each wave's two dS tiles
 // stream through three LDS buffers by direct global->LDS loads, two stages in
-// flight while one is consumed (the loop is bound by load latency, not MFMA).
+// flight while one is consumed.  The kernel is bound by the HBM reads of the
+// stored dS (about B Hq L G bytes), not by its MFMA work.
 //   dQ^T += K^T dS^T   (A: transposed reads of the K tile; B: transposed
 //                        reads of the dS^T tiles, in the same key order)
 // ---------------------------------------------------------------------------
 constexpr int DQS_WAVES = 8;
 constexpr int DQS_BQ = 32 * DQS_WAVES;
-constexpr int DQS_BK = 64;
-constexpr int DQS_NBUF = 3;  // stages in LDS: two in flight while one is consumed
-
-// Wait until at most n (wave-uniform, 0..7) vector memory operations are in flight.
-__device__ __forceinline__ void wait_vmem_upto(int n) {
-    switch (n) {
-        case 0: wait_vmem_n<0>(); break;
-        case 1: wait_vmem_n<1>(); break;
-        case 2: wait_vmem_n<2>(); break;
-        case 3: wait_vmem_n<3>(); break;
-        case 4: wait_vmem_n<4>(); break;
-        case 5: wait_vmem_n<5>(); break;
-        case 6: wait_vmem_n<6>(); break;
-        default: wait_vmem_n<7>(); break;
-    }
-}
+// Keys per stage and stages in LDS; NBUF - 1 stages are in flight while one
+// is consumed.
+template <int D> constexpr int dqs_bk() { return 64; }
+template <int D> constexpr int dqs_nbuf() { return 3; }
 
 template <int D, bool GRAD_F32>
 __global__ __launch_bounds__(64 * DQS_WAVES) void bwd_dq_ds_kernel(Params p, int n_qt) {
     constexpr int CB = D / 32;
-    constexpr int KTILE = DQS_BK * D * 2;      // one K tile
+    constexpr int BK = dqs_bk<D>();
+    constexpr int NBUF = dqs_nbuf<D>();
+    constexpr int KT32 = BK / 32;              // dS tiles per wave per stage
+    constexpr int KTILE = BK * D * 2;          // one K tile
     constexpr int KNCH = KTILE / 1024;
-    constexpr int DSW = 2 * 2048;              // a wave's two dS^T tiles
+    constexpr int DSW = KT32 * 2048;           // a wave's dS tiles of one stage
     constexpr int STAGE = KTILE + DQS_WAVES * DSW;
-    static_assert(KNCH % DQS_WAVES == 0, "K chunks per wave");
-    __shared__ __attribute__((aligned(1024))) char smem[DQS_NBUF * STAGE];
+    static_assert(BK % 32 == 0 && KNCH % DQS_WAVES == 0 && NBUF >= 2, "stage shape");
+    static_assert(NBUF * STAGE >= DQS_WAVES * 32 * D * 2, "epilogue staging fits");
+    __shared__ __attribute__((aligned(1024))) char smem[NBUF * STAGE];
 
     const int n_units = p.B * p.Hq * p.n_g;
     const Work w = decode_work(blockIdx.x, n_units, n_qt, p.Hq, p.n_g);
@@ -628,7 +654,7 @@ __global__ __launch_bounds__(64 * DQS_WAVES) void bwd_dq_ds_kernel(Params p, int
     const int q32 = qw >> 5;
     const bool wave_valid = qw < p.G;   // the wave owns queries of the group
     const int q_end = min(q0 + DQS_BQ, p.G);
-    const int n_kt = (q_end + DQS_BK - 1) / DQS_BK;
+    const int n_kt = (q_end + BK - 1) / BK;
     const size_t T = (p.G + 31) / 32;
     const char* ds_unit = static_cast<const char*>(p.ds) +
                           (((size_t)w.b * p.Hq + w.h) * p.n_g + w.g) * (T * (T + 1) / 2) * 2048;
@@ -637,23 +663,27 @@ __global__ __launch_bounds__(64 * DQS_WAVES) void bwd_dq_ds_kernel(Params p, int
     const size_t plane = ((size_t)w.b * p.L * p.Hkv + hk) * D;
     // Loads this wave issues for stage kt (uniform across the wave).
     auto n_loads = [&](int kt) {
-        return KNCH / DQS_WAVES + (wave_valid ? 2 * ((2 * kt <= q32) + (2 * kt + 1 <= q32)) : 0);
+        int n = KNCH / DQS_WAVES;
+        if (wave_valid)
+#pragma unroll
+            for (int sb = 0; sb < KT32; ++sb) n += KT32 * kt + sb <= q32 ? 2 : 0;
+        return n;
     };
-    // K tile kt and this wave's dS^T tiles (key tiles 2kt, 2kt + 1 when they
-    // are at or before its queries) -> buffer `buf`.
-    auto stage = [&](int kt, int buf) {
-        char* base = smem + buf * STAGE;
+    // K tile kt and this wave's dS tiles (key tiles KT32 kt + sb when they
+    // are at or before its queries) -> buffer `b`.
+    auto stage = [&](int kt, int b) {
+        char* base = smem + b * STAGE;
 #pragma unroll
         for (int j = 0; j < KNCH / DQS_WAVES; ++j) {
             const int cc = wave + DQS_WAVES * j;
             const ChunkSlot sl = chunk_slot<D>(cc, lane);
-            const uint32_t off = row_off(w.g, p.G, kt * DQS_BK + sl.row, s, p.L, rowb) + sl.colb;
+            const uint32_t off = row_off(w.g, p.G, kt * BK + sl.row, s, p.L, rowb) + sl.colb;
             dma16(k + plane, off, base + cc * 1024);
         }
         if (wave_valid) {
 #pragma unroll
-            for (int sb = 0; sb < 2; ++sb) {
-                const int k32 = 2 * kt + sb;
+            for (int sb = 0; sb < KT32; ++sb) {
+                const int k32 = KT32 * kt + sb;
                 if (k32 <= q32) {
                     const char* tile = ds_unit + ((size_t)q32 * (q32 + 1) / 2 + k32) * 2048;
                     char* dst = base + KTILE + wave * DSW + sb * 2048;
@@ -663,28 +693,33 @@ __global__ __launch_bounds__(64 * DQS_WAVES) void bwd_dq_ds_kernel(Params p, int
             }
         }
     };
-    stage(0, 0);
-    if (n_kt > 1) stage(1, 1);
+#pragma unroll
+    for (int j = 0; j < NBUF - 1; ++j)
+        if (j < n_kt) stage(j, j);
 
     f32x16 dq[CB];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) dq[cb] = f32x16{};
 
-    int buf = 0;  // kt % DQS_NBUF
+    int buf = 0;  // kt % NBUF
     for (int kt = 0; kt < n_kt; ++kt) {
-        // Stage kt landed (stage kt + 1, issued after it, may still be in
-        // flight); after the barrier every wave has also finished reading the
-        // buffer that stage kt + 2 overwrites (consumed at step kt - 1).
-        wait_vmem_upto(kt + 1 < n_kt ? n_loads(kt + 1) : 0);
+        // Stage kt landed (stages kt + 1 .. kt + NBUF - 2, issued after it,
+        // may still be in flight); after the barrier every wave has also
+        // finished reading the buffer that stage kt + NBUF - 1 overwrites
+        // (consumed at step kt - 1).
+        int pending = 0;
+#pragma unroll
+        for (int j = 1; j < NBUF - 1; ++j) pending += kt + j < n_kt ? n_loads(kt + j) : 0;
+        wait_vmem_upto(pending);
         __syncthreads();
-        if (kt + 2 < n_kt) stage(kt + 2, buf == 0 ? 2 : buf - 1);
+        if (kt + NBUF - 1 < n_kt) stage(kt + NBUF - 1, buf == 0 ? NBUF - 1 : buf - 1);
         const char* sK = smem + buf * STAGE;
-        buf = buf == DQS_NBUF - 1 ? 0 : buf + 1;
-        if (!wave_valid || 2 * kt > q32) continue;
-        const int n_kk = 2 * kt + 1 <= q32 ? 4 : 2;  // 16-key steps with stored dS
+        buf = buf == NBUF - 1 ? 0 : buf + 1;
+        if (!wave_valid || KT32 * kt > q32) continue;
+        const int n_kk = 2 * min(KT32, q32 - KT32 * kt + 1);  // 16-key steps with stored dS
         const char* sD = sK + KTILE + wave * DSW;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
+        for (int kk = 0; kk < 2 * KT32; ++kk) {
             if (kk >= n_kk) break;
             // B: dS^T rows (keys) 16kk + 4hh + {0..3, 8..11}, column = this
             // lane's query (see Params::ds for where key r, quad c sits).
