@@ -71,9 +71,6 @@ hipError_t launch_bwd_dkdv_f32(const Params& p, hipStream_t s);
 hipError_t launch_bwd_dq_f32(const Params& p, hipStream_t s);
 hipError_t launch_rope_prepass(const Params& p, void* q_out, void* k_out, hipStream_t s);
 
-// fp32 -> bf16 (round to nearest even), n elements.
-hipError_t launch_f32_to_bf16(const float* in, void* out, size_t n, hipStream_t s);
-
 // The checks s2attn_fwd_ex (is_bwd = 0) or s2attn_bwd_ex (is_bwd = 1) run on
 // their sizes and options, without pointers: for callers that must validate
 // a whole sequence of work before enqueueing any of it.

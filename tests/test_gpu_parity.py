@@ -417,3 +417,26 @@ def test_workspace_writes_stay_inside(rope):
         torch.cuda.synchronize()
         check("dq (recompute path)", host(pq), rdq, BF16_REL_F, bf16_store_tol(rdq))
         assert torch.equal(pk, dk) and torch.equal(pv, dv)   # same dK/dV kernel
+
+
+@pytest.mark.parametrize("rope", [None, (10000.0, 64)])
+def test_backward_stages_equal_one_call(rope):
+    """PRE, DKDV, DQ through s2attn_bwd_stage_ex, in that order on one stream,
+    give bitwise the gradients of one s2attn_bwd_ex call (the DQ stage reads
+    the dS tiles DKDV left in the workspace)."""
+    B, L, Hq, Hkv, d, G, sh = 1, 600, 4, 2, 128, 200, 2
+    say(f"[stages] rope={rope}")
+    q, k, v, do = rand_inputs(41, B, L, Hq, Hkv, d)
+    tq, tk, tv, tdo = (dev(x, BF) for x in (q, k, v, do))
+    o, lse = s2.forward(tq, tk, tv, G, sh, rope=rope)
+    ref = s2.backward(tq, tk, tv, o, lse, tdo, G, sh, rope=rope)
+    opts = s2.make_opts(BF, rope=rope)
+    n = s2.s2attn_workspace_size(1, B, L, Hq, Hkv, d, G, opts)
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dq, dk, dv = (torch.empty_like(x) for x in (tq, tk, tv))
+    for stage in (s2.S2ATTN_BWD_STAGE_PRE, s2.S2ATTN_BWD_STAGE_DKDV, s2.S2ATTN_BWD_STAGE_DQ):
+        s2.s2attn_bwd_stage_ex(stage, tq, tk, tv, o, lse, tdo, dq, dk, dv, B, L, Hq, Hkv, d, G, sh,
+                               opts, ws, n)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
+        assert torch.equal(a, b), name
