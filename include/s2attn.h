@@ -106,7 +106,7 @@ int s2attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  * Backward, bf16 inputs and gradients, scale 1/sqrt(d), no RoPE.
  * Reads q, k, v, o, lse (as written by s2attn_fwd on the same inputs) and
  * dout; writes dq, dk, dv.  delta_ws is caller scratch of 2*B*Hq*L floats
- * (receives rowsum(dout * o) and lse * log2(e), each [B, Hq, L]).  Gradient formulas: with P the attention
+ * (receives -rowsum(dout * o) and lse * log2(e), each [B, Hq, L]).  Gradient formulas: with P the attention
  * probabilities, dS = P * (dout . v_j - delta), dq = scale dS k,
  * dk = scale dS^T q, dv = P^T dout (summed over query heads per KV head).
  */
@@ -121,7 +121,7 @@ int s2attn_bwd(const void* q, const void* k, const void* v, const void* o,
  * (0 when none).  is_bwd selects the backward.  Returns 0 for invalid
  * arguments as well; the _ex call then reports the error.
  *
- * Backward workspace, each part 256-byte aligned: delta and lse * log2(e)
+ * Backward workspace, each part 256-byte aligned: -delta and lse * log2(e)
  * (2 B Hq L floats); with RoPE the rotated q and k (bf16, the sizes of q and
  * k); for bf16 inputs, the dS tiles: per (batch, head, group) the 32 x 32
  * tiles on or below the causal diagonal, T (T + 1) / 2 tiles of 2 KB with
@@ -148,7 +148,7 @@ int s2attn_bwd_ex(const void* q, const void* k, const void* v, const void* o,
 /*
  * The backward as its three kernels, for callers that time or overlap them.
  * Arguments are those of s2attn_bwd_ex, with the same workspace.
- *   S2ATTN_BWD_STAGE_PRE   delta = rowsum(dout * o) into the workspace (and,
+ *   S2ATTN_BWD_STAGE_PRE   -delta = -rowsum(dout * o) into the workspace (and,
  *                          with RoPE, the rotated q and k).
  *   S2ATTN_BWD_STAGE_DKDV  dk, dv (and, bf16, the dS tiles into the
  *                          workspace when it holds them).  Needs PRE complete.

@@ -20,7 +20,7 @@ struct Params {
     void* dq;
     void* dk;
     void* dv;
-    float* delta;   // [B, Hq, L] rowsum(dout * o), then [B, Hq, L] lse * log2(e)
+    float* delta;   // [B, Hq, L] -rowsum(dout * o), then [B, Hq, L] lse * log2(e)
     float* lse2;
     // dS tiles of the backward (null: dQ recomputes S and dP).  For unit
     // (b, h, g), tile (q32, k32) with k32 <= q32 < ceil(G/32) holds dS of

@@ -14,8 +14,10 @@
 namespace s2 {
 
 // ---------------------------------------------------------------------------
-// delta[b, h, t] = sum_c dO[b, t, h, c] * O[b, t, h, c]   (fp32), and the
-// LSE in base 2, lse2[b, h, t] = lse[b, h, t] * log2(e), for exp2 in the loops.
+// The row term, stored negated: p.delta[b, h, t] = -sum_c dO[b, t, h, c] *
+// O[b, t, h, c] (fp32; the dK/dV kernel starts its dP accumulation from it,
+// so the MFMA yields dP - delta directly), and the LSE in base 2,
+// lse2[b, h, t] = lse[b, h, t] * log2(e), for exp2 in the loops.
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(Params p, long n_rows) {
@@ -39,7 +41,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(Params p, long n_rows) {
         const int t = (int)(bt % p.L);
         const int b = (int)(bt / p.L);
         const size_t li = lse_idx(p, b, h, t);
-        p.delta[li] = acc;
+        p.delta[li] = -acc;
         p.lse2[li] = p.lse[li] * kLog2e;
     }
 }
@@ -362,7 +364,15 @@ __global__ __launch_bounds__(64 * DKV_WAVES) void bwd_dkdv_bf16_kernel(Params p,
         const float* s_l2 = reinterpret_cast<const float*>(bufs + (it & 1) * BUF + 2 * TILE) + 32 * qh;
         const float* s_dl = s_l2 + DKV_BQ;
 
-        f32x16 sacc = f32x16{}, pacc = f32x16{};
+        // dP accumulates onto -delta of its query row (element i is row
+        // 8(i/4) + 4hh + i%4), so pacc ends as dP - delta.
+        f32x16 sacc = f32x16{}, pacc;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const f32x4 d4 = *reinterpret_cast<const f32x4*>(&s_dl[8 * j + 4 * hh]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) pacc[4 * j + e] = d4[e];
+        }
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const int off = tile_off<D>(l32, 16 * ks + 8 * hh);
@@ -376,7 +386,6 @@ __global__ __launch_bounds__(64 * DKV_WAVES) void bwd_dkdv_bf16_kernel(Params p,
             for (int j = 0; j < 4; ++j) {
                 const int r0 = 8 * j + 4 * hh;
                 const f32x4 l4 = *reinterpret_cast<const f32x4*>(&s_l2[r0]);
-                const f32x4 d4 = *reinterpret_cast<const f32x4*>(&s_dl[r0]);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int i = 4 * j + e;
@@ -386,7 +395,7 @@ __global__ __launch_bounds__(64 * DKV_WAVES) void bwd_dkdv_bf16_kernel(Params p,
                         if (kj > qq || qq >= p.G) pv = 0.f;
                     }
                     sacc[i] = pv;
-                    pacc[i] = pv * (pacc[i] - d4[e]);
+                    pacc[i] = pv * pacc[i];
                 }
             }
         };
@@ -567,7 +576,7 @@ __global__ __launch_bounds__(64 * DQ_WAVES) void bwd_dq_bf16_kernel(Params p, in
                         const int key = k0 + 32 * mb + 8 * (i >> 2) + 4 * hh + (i & 3);
                         if (key > qi) pv = 0.f;
                     }
-                    pacc[mb][i] = pv * (pacc[mb][i] - dl);
+                    pacc[mb][i] = pv * (pacc[mb][i] + dl);  // dl = -delta
                 }
         };
         if (diag)
@@ -809,7 +818,7 @@ __global__ __launch_bounds__(F32_ROWS) void bwd_dq_f32_kernel(Params p, int n_qt
                 dp = fmaf(gr[c], sV[j][c], dp);
             }
             const float pv = expf(sd * p.scale - lse);
-            const float ds = pv * (dp - dl) * p.scale;
+            const float ds = pv * (dp + dl) * p.scale;  // dl = -delta
 #pragma unroll
             for (int c = 0; c < D; ++c) acc[c] = fmaf(ds, sK[j][c], acc[c]);
         }
@@ -881,7 +890,7 @@ __global__ __launch_bounds__(F32_ROWS) void bwd_dkdv_f32_kernel(Params p, int n_
                     dp = fmaf(sG[i][c], vr[c], dp);
                 }
                 const float pv = expf(sd * p.scale - sL[i]);
-                const float ds = pv * (dp - sD[i]) * p.scale;
+                const float ds = pv * (dp + sD[i]) * p.scale;  // sD = -delta
 #pragma unroll
                 for (int c = 0; c < D; ++c) {
                     dv[c] = fmaf(pv, sG[i][c], dv[c]);
