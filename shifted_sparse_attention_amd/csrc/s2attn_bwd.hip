@@ -224,7 +224,7 @@ __device__ __forceinline__ void reduce_store(const Params& p, f32x16 (&acc)[D / 
 // tile into its first and second 32 queries; each keeps partial dK, dV for
 // its keys, and the two halves are summed through LDS at the end.  The K and
 // V rows of the workgroup's keys sit in LDS for the whole kernel (MFMA B
-// operands).  The workgroup walks the query heads sharing the KV head and,
+// operands; half of each wave's K fragments are also kept in registers).  The workgroup walks the query heads sharing the KV head and,
 // for each, the 64-query tiles at or after its keys; Q, dO, LSE and delta of
 // the next tile stream into the other of two LDS buffers while the current
 // one is consumed.
@@ -293,9 +293,6 @@ __global__ __launch_bounds__(64 * DKV_WAVES) void bwd_dkdv_bf16_kernel(Params p,
     // past the group are clamped to its last row and masked in the loop.
     constexpr int NSLOT = 2 * NCH / DKV_WAVES;  // 1 KB chunks per wave per tile; Q first, then dO
     const uint32_t qrowb = (uint32_t)p.Hq * D * 2;
-    ChunkSlot slot[NSLOT];
-#pragma unroll
-    for (int j = 0; j < NSLOT; ++j) slot[j] = chunk_slot<D>((wave + DKV_WAVES * j) % NCH, lane);
     auto stage = [&](int h, int t, int buf) {
         char* base = bufs + buf * BUF;
         const int q0 = (qt_first + t) * DKV_BQ;
@@ -304,7 +301,8 @@ __global__ __launch_bounds__(64 * DKV_WAVES) void bwd_dkdv_bf16_kernel(Params p,
         for (int j = 0; j < NSLOT; ++j) {
             const bool isg = j >= NSLOT / 2;
             const int cc = (wave + DKV_WAVES * j) % NCH;
-            const uint32_t off = row_off(w.g, p.G, q0 + slot[j].row, s, p.L, qrowb) + slot[j].colb;
+            const ChunkSlot sl = chunk_slot<D>(cc, lane);  // recomputed: frees registers for kreg
+            const uint32_t off = row_off(w.g, p.G, q0 + sl.row, s, p.L, qrowb) + sl.colb;
             dma16((isg ? dout : q) + plane, off, base + (isg ? TILE : 0) + cc * 1024);
         }
         if (wave < 2) {  // LSE (base 2) and delta of the tile's 64 queries
@@ -314,6 +312,16 @@ __global__ __launch_bounds__(64 * DKV_WAVES) void bwd_dkdv_bf16_kernel(Params p,
         }
     };
     stage(hk * p.r, 0, 0);
+
+    // The first KREG channel blocks of this wave's K rows stay in registers
+    // (the B operands of S for k-steps ks < KREG): fewer LDS reads per step,
+    // within the register budget of two waves per SIMD.
+    constexpr int KREG = KS / 2;
+    bf16x8 kreg[KREG];
+    wait_vmem();
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < KREG; ++ks) kreg[ks] = ld_lds16(sKt, tile_off<D>(32 * kg + l32, 16 * ks + 8 * hh));
 
     f32x16 dk[CB], dv[CB];
 #pragma unroll
@@ -377,7 +385,8 @@ __global__ __launch_bounds__(64 * DKV_WAVES) void bwd_dkdv_bf16_kernel(Params p,
         for (int ks = 0; ks < KS; ++ks) {
             const int off = tile_off<D>(l32, 16 * ks + 8 * hh);
             const int koff = tile_off<D>(32 * kg + l32, 16 * ks + 8 * hh);
-            sacc = mfma32(ld_lds16(sQ, off), ld_lds16(sKt, koff), sacc);
+            const bf16x8 kf = ks < KREG ? kreg[ks < KREG ? ks : 0] : ld_lds16(sKt, koff);
+            sacc = mfma32(ld_lds16(sQ, off), kf, sacc);
             pacc = mfma32(ld_lds16(sO, off), ld_lds16(sVt, koff), pacc);
         }
         // P and dS; element i is query qb + 8(i/4) + 4hh + i%4 and key kj.
