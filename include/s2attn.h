@@ -124,9 +124,10 @@ int s2attn_bwd(const void* q, const void* k, const void* v, const void* o,
  * Backward workspace, each part 256-byte aligned: -delta and lse * log2(e)
  * (2 B Hq L floats); with RoPE the rotated q and k (bf16, the sizes of q and
  * k); for bf16 inputs, the dS tiles: per (batch, head, group) the 32 x 32
- * tiles on or below the causal diagonal, T (T + 1) / 2 tiles of 2 KB with
- * T = ceil(G / 32), i.e. B Hq (L / G) T (T + 1) / 2 * 2048 bytes (about
- * B Hq L G bytes), kept only while that is at most 32 GiB.  The dK/dV kernel
+ * tiles on or below the causal diagonal, padded to whole blocks of 8 query
+ * rows: 32 NB (NB + 1) tiles of 2 KB with NB = ceil(ceil(G / 32) / 8), i.e.
+ * B Hq (L / G) 32 NB (NB + 1) * 2048 bytes (about B Hq L G bytes), kept only
+ * while that is at most 32 GiB.  The dK/dV kernel
  * writes dS there and the dQ kernel reads it, so dQ is one product instead
  * of recomputing the scores; above the bound dQ recomputes them.  The plain
  * s2attn_bwd has no workspace and always recomputes.

@@ -23,13 +23,16 @@ struct Params {
     float* delta;   // [B, Hq, L] -rowsum(dout * o), then [B, Hq, L] lse * log2(e)
     float* lse2;
     // dS tiles of the backward (null: dQ recomputes S and dP).  For unit
-    // (b, h, g), tile (q32, k32) with k32 <= q32 < ceil(G/32) holds dS of
-    // queries 32 q32 .. +31 against keys 32 k32 .. +31, 2 KB at byte
-    // (unit * T (T + 1) / 2 + q32 (q32 + 1) / 2 + k32) * 2048 with
-    // T = ceil(G / 32) and unit = (b Hq + h) n_g + g.  Within a tile, the
-    // four bf16 of key r (0..31) and query quad c (queries 4c .. 4c+3) sit at
-    // byte 1024 (c >> 2) + 16 (r + 32 (c & 1)) + 8 ((c >> 1) & 1): the order
-    // the dK/dV kernel holds them in registers.
+    // (b, h, g), tile (q32, k32) with k32 <= q32 < T = ceil(G/32) holds dS of
+    // queries 32 q32 .. +31 against keys 32 k32 .. +31, 2 KB.  Query rows go
+    // in blocks of 8 (t = q32 / 8), each block stored k32-major over its
+    // 8 (t + 1) key tiles: tile (q32, k32) is number 32 t (t + 1) + 8 k32 +
+    // q32 % 8 of the unit, whose UT = 32 NB (NB + 1) tiles (NB = ceil(T / 8))
+    // start at tile (b Hq + h) n_g + g) * UT.  So the 8 rows one dQ
+    // workgroup reads advance through consecutive memory.  Within a tile,
+    // the four bf16 of key r (0..31) and query quad c (queries 4c .. 4c+3)
+    // sit at byte 1024 (c >> 2) + 16 (r + 32 (c & 1)) + 8 ((c >> 1) & 1): the
+    // order the dK/dV kernel holds them in registers.
     void* ds;
     // Sizes.
     int B, L, Hq, Hkv, d, G, shifted_heads;

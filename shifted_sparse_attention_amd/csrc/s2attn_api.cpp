@@ -78,8 +78,8 @@ size_t elem_size(int dtype) { return dtype == S2ATTN_F32 ? 4 : 2; }
 constexpr double kMaxDsBytes = 32.0 * (1ull << 30);
 
 size_t ds_bytes(int B, int Hq, int L, int G) {
-    const size_t T = ((size_t)G + 31) / 32;
-    return (size_t)B * Hq * (L / G) * (T * (T + 1) / 2) * 2048;
+    const size_t NB = (((size_t)G + 31) / 32 + 7) / 8;   // blocks of 8 query rows
+    return (size_t)B * Hq * (L / G) * (32 * NB * (NB + 1)) * 2048;
 }
 
 bool use_ds(int B, int Hq, int L, int G, const Resolved& r) {

@@ -13,6 +13,17 @@
 
 namespace s2 {
 
+// dS tile layout (see Params::ds): tiles per (batch, head, group) unit, and
+// the number of tile (q32, k32), k32 <= q32, within its unit.
+__device__ __forceinline__ size_t ds_unit_tiles(int G) {
+    const size_t nb = ((size_t)(G + 31) / 32 + 7) / 8;
+    return 32 * nb * (nb + 1);
+}
+__device__ __forceinline__ size_t ds_tile(int q32, int k32) {
+    const size_t t = (size_t)(q32 >> 3);
+    return 32 * t * (t + 1) + 8 * (size_t)k32 + (q32 & 7);
+}
+
 // ---------------------------------------------------------------------------
 // The row term, stored negated: p.delta[b, h, t] = -sum_c dO[b, t, h, c] *
 // O[b, t, h, c] (fp32; the dK/dV kernel starts its dP accumulation from it,
@@ -330,10 +341,10 @@ __global__ __launch_bounds__(64 * DKV_WAVES) void bwd_dkdv_bf16_kernel(Params p,
         dv[cb] = f32x16{};
     }
 
-    // dS tiles of the current query head (see Params::ds): the head's base
+    // dS tiles of the current query head (see Params::ds): the head's base,
     // and the tile of this wave's keys in query row q32 at
-    // + (q32 (q32 + 1) / 2 + kw / 32) * 2048.
-    const size_t TT = ((size_t)(p.G + 31) / 32) * ((p.G + 31) / 32 + 1) / 2;
+    // + ds_tile(q32, kw / 32) * 2048.
+    const size_t TT = ds_unit_tiles(p.G);
     auto ds_head = [&](int h) {
         return p.ds == nullptr ? nullptr
                                : static_cast<char*>(p.ds) +
@@ -428,9 +439,7 @@ __global__ __launch_bounds__(64 * DKV_WAVES) void bwd_dkdv_bf16_kernel(Params p,
             // dS tile out for the dQ kernel, in register order: db[kk] of
             // every lane at byte 1024 kk + 16 lane, so each store writes 1 KB
             // of whole cache lines.  Streaming (non-temporal): it is read once.
-            const uint32_t q32 = qb >> 5, k32 = kw >> 5;
-            const size_t tile = (size_t)q32 * (q32 + 1) / 2 + k32;
-            u32x4* out = reinterpret_cast<u32x4*>(it_ds + tile * 2048) + lane;
+            u32x4* out = reinterpret_cast<u32x4*>(it_ds + ds_tile(qb >> 5, kw >> 5) * 2048) + lane;
             __builtin_nontemporal_store(__builtin_bit_cast(u32x4, db[0]), out);
             __builtin_nontemporal_store(__builtin_bit_cast(u32x4, db[1]), out + 64);
             ds_inflight = 2;
@@ -673,9 +682,8 @@ __global__ __launch_bounds__(64 * DQS_WAVES) void bwd_dq_ds_kernel(Params p, int
     const bool wave_valid = qw < p.G;   // the wave owns queries of the group
     const int q_end = min(q0 + DQS_BQ, p.G);
     const int n_kt = (q_end + BK - 1) / BK;
-    const size_t T = (p.G + 31) / 32;
     const char* ds_unit = static_cast<const char*>(p.ds) +
-                          (((size_t)w.b * p.Hq + w.h) * p.n_g + w.g) * (T * (T + 1) / 2) * 2048;
+                          (((size_t)w.b * p.Hq + w.h) * p.n_g + w.g) * ds_unit_tiles(p.G) * 2048;
 
     const uint32_t rowb = (uint32_t)p.Hkv * D * 2;
     const size_t plane = ((size_t)w.b * p.L * p.Hkv + hk) * D;
@@ -703,7 +711,7 @@ __global__ __launch_bounds__(64 * DQS_WAVES) void bwd_dq_ds_kernel(Params p, int
             for (int sb = 0; sb < KT32; ++sb) {
                 const int k32 = KT32 * kt + sb;
                 if (k32 <= q32) {
-                    const char* tile = ds_unit + ((size_t)q32 * (q32 + 1) / 2 + k32) * 2048;
+                    const char* tile = ds_unit + ds_tile(q32, k32) * 2048;
                     char* dst = base + KTILE + wave * DSW + sb * 2048;
                     dma16(tile, 16u * lane, dst);
                     dma16(tile + 1024, 16u * lane, dst + 1024);

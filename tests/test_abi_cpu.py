@@ -153,15 +153,19 @@ def test_workspace_sizes_and_checks():
     assert s2.s2attn_workspace_size(0, B, Ln, Hq, Hkv, d, G, o) == 0
     r256 = lambda x: (x + 255) // 256 * 256
     delta = 2 * B * Hq * Ln * 4     # delta and lse * log2(e)
-    # dS tiles: per (batch, head, group) the 32 x 32 bf16 tiles of the causal triangle
-    T = (G + 31) // 32
-    ds = B * Hq * (Ln // G) * (T * (T + 1) // 2) * 2048
+    # dS tiles: per (batch, head, group) the 32 x 32 bf16 tiles of the causal
+    # triangle, padded to whole blocks of 8 query rows (NB blocks)
+    def ds_bytes(B, Hq, L, G):
+        NB = ((G + 31) // 32 + 7) // 8
+        return B * Hq * (L // G) * 32 * NB * (NB + 1) * 2048
+    ds = ds_bytes(B, Hq, Ln, G)
     assert s2.s2attn_workspace_size(1, B, Ln, Hq, Hkv, d, G, o) == r256(delta) + r256(ds)
     o.dtype = o.grad_dtype = s2.S2ATTN_F32   # fp32 backward recomputes dS: no tiles
     assert s2.s2attn_workspace_size(1, B, Ln, Hq, Hkv, d, G, o) == r256(delta)
     o.dtype = o.grad_dtype = s2.S2ATTN_BF16
-    Gr = 80                          # ragged last tile row (T = 3)
-    dsr = B * Hq * (240 // Gr) * 6 * 2048
+    Gr = 80                          # ragged last tile row (T = 3, one block of 8 rows)
+    dsr = ds_bytes(B, Hq, 240, Gr)
+    assert dsr == B * Hq * 3 * 64 * 2048
     assert s2.s2attn_workspace_size(1, B, 240, Hq, Hkv, d, Gr, o) == r256(2 * B * Hq * 240 * 4) + r256(dsr)
     o.rope = 1
     rq, rk = B * Ln * Hq * d * 2, B * Ln * Hkv * d * 2
