@@ -77,13 +77,21 @@ size_t elem_size(int dtype) { return dtype == S2ATTN_F32 ? 4 : 2; }
 // recomputes S and dP instead.
 constexpr double kMaxDsBytes = 32.0 * (1ull << 30);
 
-size_t ds_bytes(int B, int Hq, int L, int G) {
-    const size_t NB = (((size_t)G + 31) / 32 + 7) / 8;   // blocks of 8 query rows
-    return (size_t)B * Hq * (L / G) * (32 * NB * (NB + 1)) * 2048;
+// Bytes of the dS tiles (blocks of 8 query rows, see Params::ds), in double so
+// the bound check cannot wrap for any accepted size.
+double ds_bytes_f(int B, int Hq, int L, int G) {
+    const double NB = (double)((((size_t)G + 31) / 32 + 7) / 8);
+    return (double)B * Hq * (L / G) * (32.0 * NB * (NB + 1)) * 2048.0;
 }
 
 bool use_ds(int B, int Hq, int L, int G, const Resolved& r) {
-    return r.dtype == S2ATTN_BF16 && (double)ds_bytes(B, Hq, L, G) <= kMaxDsBytes;
+    return r.dtype == S2ATTN_BF16 && ds_bytes_f(B, Hq, L, G) <= kMaxDsBytes;
+}
+
+// Exact byte count; called only when use_ds holds (at most 32 GiB).
+size_t ds_bytes(int B, int Hq, int L, int G) {
+    const size_t NB = (((size_t)G + 31) / 32 + 7) / 8;
+    return (size_t)B * Hq * (L / G) * (32 * NB * (NB + 1)) * 2048;
 }
 
 // Workspace layout: [row terms (bwd): delta and lse*log2(e) | rotated q | rotated k |
