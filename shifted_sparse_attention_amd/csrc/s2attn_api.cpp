@@ -94,7 +94,7 @@ size_t ds_bytes(int B, int Hq, int L, int G) {
     return (size_t)B * Hq * (L / G) * (32 * NB * (NB + 1)) * 2048;
 }
 
-// Workspace layout: [row terms (bwd): delta and lse*log2(e) | rotated q | rotated k |
+// Workspace layout: [row terms (bwd): -delta and lse*log2(e) | rotated q | rotated k |
 // dS tiles (bwd, when kept)], each 256-byte aligned.
 struct WsLayout {
     size_t delta_off, delta_bytes;
