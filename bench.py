@@ -188,6 +188,13 @@ def main():
     ms_step = start.elapsed_time(end) / args.steps
     names = ["fwd", "bwd_pre", "bwd_dkdv", "bwd_dq"][:n_ev - 1]
     kms = {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, n in enumerate(names)}
+    # Per-step spans (events on the launch stream): forward, backward, both.
+    spans = {"fwd": [e[0].elapsed_time(e[1]) for e in evs]}
+    if wl.backward:
+        spans["bwd"] = [e[1].elapsed_time(e[n_ev - 1]) for e in evs]
+        spans["fwd_bwd"] = [e[0].elapsed_time(e[n_ev - 1]) for e in evs]
+    span_stats = {k: {"median": round(float(np.median(v)), 4), "min": round(float(np.min(v)), 4)}
+                  for k, v in spans.items()}
 
     if args.copy_probe_mb:
         n = args.copy_probe_mb * (1 << 20)
@@ -229,6 +236,7 @@ def main():
                    "parallelism": "single GPU"},
         "pct_of_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "kernels_ms": {k: round(v, 4) for k, v in kms.items()},
+        "step_spans_ms": span_stats,
         "roofline": {
             "kernel": dom,
             "bound": "mfma",
@@ -304,6 +312,10 @@ def bench_block(args, wl):
     ms_step = start.elapsed_time(end) / args.steps
     kms = {"block_fwd": float(np.mean([e[0].elapsed_time(e[1]) for e in evs])),
            "block_bwd": float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))}
+    spans = {"fwd": [e[0].elapsed_time(e[1]) for e in evs], "bwd": [e[1].elapsed_time(e[2]) for e in evs],
+             "fwd_bwd": [e[0].elapsed_time(e[2]) for e in evs]}
+    span_stats = {k: {"median": round(float(np.median(v)), 4), "min": round(float(np.min(v)), 4)}
+                  for k, v in spans.items()}
     ffl, bfl = F.block_flops(wl.B, wl.L, wl.Hq, wl.Hkv, wl.d, wl.G, wl.lora_rank)
     att = F.fwd_bwd_flops(wl.B, wl.L, wl.Hq, wl.d, wl.G)
     tflops = (ffl + bfl) / (ms_step * 1e-3) / 1e12
@@ -321,6 +333,7 @@ def bench_block(args, wl):
                    "rope": bool(wl.rope), "seed": wl.seed, "parallelism": "single GPU"},
         "pct_of_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "kernels_ms": {k: round(v, 4) for k, v in kms.items()},
+        "step_spans_ms": span_stats,
         "attention_flop_share": round(att / (ffl + bfl), 4),
         # The block's launches sit inside one C call each; the dominant unit
         # timed with events on its stream is the forward or the backward call.
