@@ -125,6 +125,11 @@ __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, char* ld
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                  :: "s"(lds_addr(lds_base)), "v"(voff), "s"(sbase) : "memory");
 }
+// The same with the non-temporal hint, for data read exactly once.
+__device__ __forceinline__ void dma16_nt(const void* sbase, uint32_t voff, char* lds_base) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
+                 :: "s"(lds_addr(lds_base)), "v"(voff), "s"(sbase) : "memory");
+}
 __device__ __forceinline__ void dma4(const void* sbase, uint32_t voff, char* lds_base) {
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
                  :: "s"(lds_addr(lds_base)), "v"(voff), "s"(sbase) : "memory");

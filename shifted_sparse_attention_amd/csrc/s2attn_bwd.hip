@@ -713,8 +713,8 @@ __global__ __launch_bounds__(64 * DQS_WAVES) void bwd_dq_ds_kernel(Params p, int
                 if (k32 <= q32) {
                     const char* tile = ds_unit + ds_tile(q32, k32) * 2048;
                     char* dst = base + KTILE + wave * DSW + sb * 2048;
-                    dma16(tile, 16u * lane, dst);
-                    dma16(tile + 1024, 16u * lane, dst + 1024);
+                    dma16_nt(tile, 16u * lane, dst);  // read once: streaming
+                    dma16_nt(tile + 1024, 16u * lane, dst + 1024);
                 }
             }
         }
