@@ -106,6 +106,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--flush-mb", type=int, default=0,
+                    help="overwrite a scratch buffer of this many MiB before each timed step (cold caches); "
+                         "value and ms_per_step then come from the per-step spans, which exclude the flush")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="after timing, run one device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -178,10 +181,14 @@ def main():
     n_ev = 5 if wl.backward else 2
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    flush = (torch.empty(args.flush_mb << 20, dtype=torch.uint8, device=dev)
+             if args.flush_mb > 0 else None)
     torch.cuda.synchronize()
     with ClockSampler() as clk:
         start.record(stream)
         for i in range(args.steps):
+            if flush is not None:
+                flush.fill_(i & 255)   # evicts L2 and the last-level cache before the step
             step(evs[i])
         end.record(stream)
         torch.cuda.synchronize()
@@ -195,6 +202,8 @@ def main():
         spans["fwd_bwd"] = [e[0].elapsed_time(e[n_ev - 1]) for e in evs]
     span_stats = {k: {"median": round(float(np.median(v)), 4), "min": round(float(np.min(v)), 4)}
                   for k, v in spans.items()}
+    if flush is not None:   # the flush sits between the steps: time the steps alone
+        ms_step = float(np.mean(spans["fwd_bwd" if wl.backward else "fwd"]))
 
     if args.copy_probe_mb:
         n = args.copy_probe_mb * (1 << 20)
@@ -233,7 +242,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "B": B, "L": L, "Hq": Hq, "Hkv": Hkv, "d": d, "G": G,
                    "shifted_heads": sh, "rope": bool(wl.rope), "seed": wl.seed,
-                   "parallelism": "single GPU"},
+                   "parallelism": "single GPU",
+                   "caches": f"flushed ({args.flush_mb} MiB written before each step)" if flush is not None else "warm"},
         "pct_of_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "kernels_ms": {k: round(v, 4) for k, v in kms.items()},
         "step_spans_ms": span_stats,
