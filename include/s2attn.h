@@ -52,7 +52,10 @@ typedef enum {
     S2ATTN_ERR_UNSUPPORTED = 2,  /* d not in {64, 128}; backward with shifted_heads % (Hq/Hkv)
                                     != 0 (a KV head shared by shifted and unshifted query
                                     heads); RoPE with float32 inputs; bf16 gradients of
-                                    float32 inputs; sizes whose grid exceeds 2^31 blocks */
+                                    float32 inputs; sizes past the kernels' index ranges:
+                                    a (batch, head) plane of L*H*d*2 >= 2^31 bytes,
+                                    L >= 2^24, L*Hq >= 2^31, or a grid of 2^31 or more
+                                    workgroups */
     S2ATTN_ERR_WORKSPACE = 3,    /* workspace missing or smaller than s2attn_workspace_size() */
     S2ATTN_ERR_HIP = 4           /* a HIP runtime error (no device, launch failure, ...) */
 } s2attn_status;
