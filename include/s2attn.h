@@ -48,7 +48,8 @@ typedef enum {
     S2ATTN_OK = 0,
     S2ATTN_ERR_INVALID_ARG = 1,  /* null pointer, size <= 0, L % G != 0, odd G with shifted
                                     heads, Hq % Hkv != 0, shifted_heads outside [0, Hq],
-                                    bad opts (struct_size, dtype, rope fields) */
+                                    bad opts (struct_size, dtype, rope fields,
+                                    ds_max_mib < -1) */
     S2ATTN_ERR_UNSUPPORTED = 2,  /* d not in {64, 128}; backward with shifted_heads % (Hq/Hkv)
                                     != 0 (a KV head shared by shifted and unshifted query
                                     heads); RoPE with float32 inputs; bf16 gradients of
@@ -83,6 +84,11 @@ enum {
  *                pairs (c, c + d/2), c < d/2, before attention (RoPE with
  *                position interpolation, LongLoRA blog section 3.4).
  *                Gradients are then w.r.t. the un-rotated q and k.
+ *   ds_max_mib   largest region of dS tiles, in MiB, the backward may keep in
+ *                its workspace (see s2attn_workspace_size); above it dQ
+ *                recomputes the scores instead.  -1 selects the default,
+ *                98304 (96 GiB, a third of the MI355X's HBM); 0 never keeps
+ *                dS.  Values below -1: S2ATTN_ERR_INVALID_ARG.
  */
 typedef struct {
     uint32_t struct_size;  /* must equal sizeof(s2attn_opts) */
@@ -92,9 +98,11 @@ typedef struct {
     int32_t rope;
     float rope_base;
     int32_t rope_orig_len;
+    int32_t ds_max_mib;
 } s2attn_opts;
 
-/* Defaults: bf16 inputs and gradients, scale 1/sqrt(d), no RoPE. */
+/* Defaults: bf16 inputs and gradients, scale 1/sqrt(d), no RoPE, dS kept up
+   to 96 GiB. */
 void s2attn_opts_init(s2attn_opts* opts);
 
 /*
@@ -130,10 +138,10 @@ int s2attn_bwd(const void* q, const void* k, const void* v, const void* o,
  * tiles on or below the causal diagonal, padded to whole blocks of 8 query
  * rows: 32 NB (NB + 1) tiles of 2 KB with NB = ceil(ceil(G / 32) / 8), i.e.
  * B Hq (L / G) 32 NB (NB + 1) * 2048 bytes (about B Hq L G bytes), kept only
- * while that is at most 32 GiB.  The dK/dV kernel
- * writes dS there and the dQ kernel reads it, so dQ is one product instead
- * of recomputing the scores; above the bound dQ recomputes them.  The plain
- * s2attn_bwd has no workspace and always recomputes.
+ * while that is at most opts->ds_max_mib MiB (96 GiB by default).  The dK/dV
+ * kernel writes dS there and the dQ kernel reads it, so dQ is one product
+ * instead of recomputing the scores; above the bound dQ recomputes them.  The
+ * plain s2attn_bwd has no workspace and always recomputes.
  */
 size_t s2attn_workspace_size(int is_bwd, int B, int L, int Hq, int Hkv, int d, int G,
                              const s2attn_opts* opts);

@@ -37,8 +37,10 @@ def _shapes(q, k, v):
     return B, L, Hq, k.shape[2], d
 
 
-def make_opts(dtype, grad_dtype=None, scale=None, rope=None):
-    """Build s2attn_opts.  `rope` is None or (base, orig_len)."""
+def make_opts(dtype, grad_dtype=None, scale=None, rope=None, ds_max_mib=None):
+    """Build s2attn_opts.  `rope` is None or (base, orig_len); `ds_max_mib`
+    bounds the dS tiles the backward keeps in its workspace (None: the
+    library default, 0: never)."""
     o = s2attn_opts_init()
     o.dtype = _DT[dtype]
     o.grad_dtype = _DT[grad_dtype if grad_dtype is not None else dtype]
@@ -47,6 +49,8 @@ def make_opts(dtype, grad_dtype=None, scale=None, rope=None):
         o.rope = 1
         o.rope_base = float(rope[0])
         o.rope_orig_len = int(rope[1])
+    if ds_max_mib is not None:
+        o.ds_max_mib = int(ds_max_mib)
     return o
 
 
@@ -63,8 +67,12 @@ def forward(q, k, v, G, shifted_heads, *, scale=None, rope=None, stream=None):
 
 
 def backward(q, k, v, o, lse, dout, G, shifted_heads, *, scale=None, rope=None,
-             grad_dtype=None, stream=None):
-    """S2-Attn backward.  Returns (dq, dk, dv) in `grad_dtype` (default: q's dtype)."""
+             grad_dtype=None, ds_max_mib=None, stream=None):
+    """S2-Attn backward.  Returns (dq, dk, dv) in `grad_dtype` (default: q's dtype).
+
+    The workspace it allocates holds the dS tiles (about B Hq L G bytes) unless
+    they exceed `ds_max_mib` MiB (default 96 GiB; 0: dQ recomputes instead).
+    """
     B, L, Hq, Hkv, d = _shapes(q, k, v)
     if dout.shape != q.shape or o.shape != q.shape or lse.shape != (B, Hq, L):
         raise ValueError("o and dout must match q; lse must be [B, Hq, L]")
@@ -72,7 +80,7 @@ def backward(q, k, v, o, lse, dout, G, shifted_heads, *, scale=None, rope=None,
     dq = torch.empty(q.shape, dtype=gd, device=q.device)
     dk = torch.empty(k.shape, dtype=gd, device=q.device)
     dv = torch.empty(v.shape, dtype=gd, device=q.device)
-    opts = make_opts(q.dtype, grad_dtype=gd, scale=scale, rope=rope)
+    opts = make_opts(q.dtype, grad_dtype=gd, scale=scale, rope=rope, ds_max_mib=ds_max_mib)
     ws_bytes = s2attn_workspace_size(1, B, L, Hq, Hkv, d, G, opts)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     s2attn_bwd_ex(q, k, v, o, lse, dout, dq, dk, dv, B, L, Hq, Hkv, d, G, shifted_heads,

@@ -43,6 +43,7 @@ class s2attn_opts(ctypes.Structure):
         ("rope", ctypes.c_int32),
         ("rope_base", ctypes.c_float),
         ("rope_orig_len", ctypes.c_int32),
+        ("ds_max_mib", ctypes.c_int32),
     ]
 
 

@@ -18,6 +18,12 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// The backward keeps dS (bf16, 32 x 32 tiles of each group's causal
+// triangle) for the dQ kernel while the tiles fit the caller's bound; above
+// it, dQ recomputes S and dP instead.  Default bound: 96 GiB, a third of the
+// MI355X's 288 GB of HBM.
+constexpr double kDefaultDsMaxMib = 96.0 * 1024.0;
+
 struct Resolved {
     int dtype;       // S2ATTN_BF16 / S2ATTN_F32
     int grad_dtype;
@@ -25,6 +31,7 @@ struct Resolved {
     int rope;
     float rope_base;
     int rope_orig_len;
+    double ds_max_bytes;  // dS tiles are kept in the workspace up to this size
 };
 
 // Sizes shared by forward and backward.
@@ -61,21 +68,19 @@ int resolve_opts(const s2attn_opts* o, int d, Resolved* r) {
         if (o->dtype == S2ATTN_F32) return S2ATTN_ERR_UNSUPPORTED;
     }
     if (o->dtype == S2ATTN_F32 && o->grad_dtype == S2ATTN_BF16) return S2ATTN_ERR_UNSUPPORTED;
+    if (o->ds_max_mib < -1) return S2ATTN_ERR_INVALID_ARG;
     r->dtype = o->dtype;
     r->grad_dtype = o->grad_dtype;
     r->scale = o->softmax_scale > 0.f ? o->softmax_scale : 1.0f / sqrtf((float)d);
     r->rope = o->rope ? 1 : 0;
     r->rope_base = o->rope_base;
     r->rope_orig_len = o->rope_orig_len;
+    r->ds_max_bytes = (o->ds_max_mib < 0 ? kDefaultDsMaxMib : (double)o->ds_max_mib) * 1048576.0;
     return S2ATTN_OK;
 }
 
 size_t elem_size(int dtype) { return dtype == S2ATTN_F32 ? 4 : 2; }
 
-// The backward keeps dS (bf16, 32 x 32 tiles of each group's causal
-// triangle) for the dQ kernel when it fits this bound; above it, dQ
-// recomputes S and dP instead.
-constexpr double kMaxDsBytes = 32.0 * (1ull << 30);
 
 // Bytes of the dS tiles (blocks of 8 query rows, see Params::ds), in double so
 // the bound check cannot wrap for any accepted size.
@@ -85,10 +90,11 @@ double ds_bytes_f(int B, int Hq, int L, int G) {
 }
 
 bool use_ds(int B, int Hq, int L, int G, const Resolved& r) {
-    return r.dtype == S2ATTN_BF16 && ds_bytes_f(B, Hq, L, G) <= kMaxDsBytes;
+    return r.dtype == S2ATTN_BF16 && ds_bytes_f(B, Hq, L, G) <= r.ds_max_bytes;
 }
 
-// Exact byte count; called only when use_ds holds (at most 32 GiB).
+// Exact byte count; called only when use_ds holds (within the bound, so the
+// size_t product cannot wrap).
 size_t ds_bytes(int B, int Hq, int L, int G) {
     const size_t NB = (((size_t)G + 31) / 32 + 7) / 8;
     return (size_t)B * Hq * (L / G) * (32 * NB * (NB + 1)) * 2048;
@@ -292,6 +298,7 @@ void s2attn_opts_init(s2attn_opts* opts) {
     opts->rope = 0;
     opts->rope_base = 10000.f;
     opts->rope_orig_len = 4096;
+    opts->ds_max_mib = -1;
 }
 
 int s2attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int L,

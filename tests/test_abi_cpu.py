@@ -182,6 +182,43 @@ def test_workspace_sizes_and_checks():
     assert bwd_ex(o2, None, 0, Hkv=2) == WS          # the backward always needs delta space
 
 
+def test_ds_tiles_bound():
+    """dS tiles are kept while they fit opts.ds_max_mib (default 96 GiB)."""
+    r256 = lambda x: (x + 255) // 256 * 256
+    def ds_bytes(B, Hq, L, G):
+        NB = ((G + 31) // 32 + 7) // 8
+        return B * Hq * (L // G) * 32 * NB * (NB + 1) * 2048
+    def ws(B, Ln, H, G, mib=None, rope=False):
+        o = s2.s2attn_opts_init()
+        if mib is not None:
+            o.ds_max_mib = mib
+        if rope:
+            o.rope = 1
+        return s2.s2attn_workspace_size(1, B, Ln, H, H, 128, G, o)
+    assert s2.s2attn_opts_init().ds_max_mib == -1
+    # L = 32768, G = 8192, 32 heads: 8448 MiB of tiles
+    rows = r256(2 * 32 * 32768 * 4)
+    ds32 = ds_bytes(1, 32, 32768, 8192)
+    assert ds32 == 8448 << 20
+    assert ws(1, 32768, 32, 8192) == rows + ds32
+    assert ws(1, 32768, 32, 8192, mib=8448) == rows + ds32     # exactly at the bound
+    assert ws(1, 32768, 32, 8192, mib=8447) == rows            # one MiB short: recompute
+    assert ws(1, 32768, 32, 8192, mib=0) == rows
+    # L = 102400, G = 25600 with RoPE: 78.9 GiB of tiles, under the 96 GiB default
+    rot = r256(102400 * 32 * 128 * 2)
+    ds100 = ds_bytes(1, 32, 102400, 25600)
+    assert 64 << 30 < ds100 < 96 << 30
+    assert ws(1, 102400, 32, 25600, rope=True) == r256(2 * 32 * 102400 * 4) + 2 * rot + ds100
+    assert ws(1, 102400, 32, 25600, mib=32 << 10, rope=True) == r256(2 * 32 * 102400 * 4) + 2 * rot
+    # four times that (B = 4) exceeds the default: recompute
+    assert ws(4, 102400, 32, 25600) == r256(2 * 4 * 32 * 102400 * 4)
+    # below -1 is an argument error (workspace size 0, the call reports it)
+    o = s2.s2attn_opts_init()
+    o.ds_max_mib = -2
+    assert s2.s2attn_workspace_size(1, 1, 256, 4, 4, 64, 64, o) == 0
+    assert bwd_ex(o, FAKE, 1 << 20, Hkv=2) == INV
+
+
 def test_python_wrappers_raise_named_errors():
     with pytest.raises(s2.S2AttnError) as e:
         s2.s2attn_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 256, 4, 4, 64, 60, 0)
