@@ -388,7 +388,8 @@ def test_every_output_written_and_no_stray_writes():
 def test_workspace_writes_stay_inside(rope):
     """The _ex backward writes only inside its workspace (delta, rotated q/k,
     the dS tiles of a ragged group: G = 200 leaves an 8-query last tile),
-    and the stored-dS dQ path agrees with the recomputing one of s2attn_bwd."""
+    and the stored-dS dQ path agrees with the recomputing one, reached both
+    through s2attn_bwd and through opts.ds_max_mib = 0."""
     B, L, Hq, Hkv, d, G, sh = 1, 600, 4, 2, 128, 200, 2
     say(f"[invariant] workspace redzones rope={rope}")
     q, k, v, do = rand_inputs(31, B, L, Hq, Hkv, d)
@@ -417,6 +418,15 @@ def test_workspace_writes_stay_inside(rope):
         torch.cuda.synchronize()
         check("dq (recompute path)", host(pq), rdq, BF16_REL_F, bf16_store_tol(rdq))
         assert torch.equal(pk, dk) and torch.equal(pv, dv)   # same dK/dV kernel
+    # ds_max_mib = 0: a smaller workspace without dS tiles, and dQ recomputes
+    n0 = s2.s2attn_workspace_size(1, B, L, Hq, Hkv, d, G, s2.make_opts(BF, rope=rope, ds_max_mib=0))
+    assert n0 < n
+    zq, zk, zv = s2.backward(tq, tk, tv, o, lse, tdo, G, sh, rope=rope, ds_max_mib=0)
+    torch.cuda.synchronize()
+    check("dq (ds_max_mib=0)", host(zq), rdq, BF16_REL_F, bf16_store_tol(rdq))
+    assert torch.equal(zk, dk) and torch.equal(zv, dv)
+    if rope is None:
+        assert torch.equal(zq, pq)   # the same recomputing kernel as s2attn_bwd
 
 
 @pytest.mark.parametrize("rope", [None, (10000.0, 64)])
