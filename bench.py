@@ -423,7 +423,9 @@ def cpu_baseline(wl, x, seconds):
                 "seconds": round(dt, 2)}
 
     scale = 1.0 / np.sqrt(wl.d)
-    units = [(0, h, g) for g in range(wl.n_groups) for h in (0, wl.Hq - 1, wl.Hq // 2, 1)]
+    heads = [h for h in dict.fromkeys((0, wl.Hq - 1, wl.Hq // 2, 1, wl.Hq // 4, 3 * wl.Hq // 4, 2,
+                                       wl.Hq - 2)) if 0 <= h < wl.Hq]
+    units = [(0, h, g) for h in heads for g in range(wl.n_groups)]
     done, t0 = 0, time.time()
     for b, h, g in units:
         rows = O.unit_rows(wl.L, wl.G, wl.Hq, wl.shifted_heads, h, g)
