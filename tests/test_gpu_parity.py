@@ -100,6 +100,58 @@ def test_small_f32_fwd_bwd(case):
         check(name, host(x), r, F32_TOL, F32_TOL)
 
 
+def test_growing_scores_move_the_reference_max():
+    """Scores that climb along the keys: q_i and k_j lie near one direction u,
+    k_j scaled by its in-group position, so a row's running maximum rises by
+    about 85 raw units per 128-key tile, past the forward's lazy threshold
+    (8 / (scale log2 e), 62.7 at d = 128) in nearly every tile.  O and l are
+    then rescaled mid-row again and again; outputs and gradients must still
+    match the oracle (the shifted head adds a wrap where the scores fall)."""
+    B, L, Hq, Hkv, d, G, sh = 1, 2048, 2, 2, 128, 1024, 1
+    say("[edge] growing scores")
+    rng = np.random.default_rng(77)
+    u = rng.standard_normal(d).astype(np.float32)
+    pos = (np.arange(L) % G).astype(np.float32)
+    q = u[None, None, None, :] + 0.3 * rng.standard_normal((B, L, Hq, d), dtype=np.float32)
+    k = (u[None, None, None, :] * (0.005 * pos)[None, :, None, None]
+         + 0.3 * rng.standard_normal((B, L, Hkv, d), dtype=np.float32))
+    v = rng.standard_normal((B, L, Hkv, d), dtype=np.float32)
+    do = rng.standard_normal((B, L, Hq, d), dtype=np.float32)
+    q, k, v, do = (bf16_round(x.astype(np.float32)) for x in (q, k, v, do))
+    tq, tk, tv, tdo = (dev(x, BF) for x in (q, k, v, do))
+    o, lse = s2.forward(tq, tk, tv, G, sh)
+    g32 = s2.backward(tq, tk, tv, o, lse, tdo, G, sh, grad_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rdq, rdk, rdv, ro, rlse = O.backward(q, k, v, do, G, sh)
+    assert float(np.max(rlse)) > 60.0   # the scores really do climb
+    check("o", host(o), ro, BF16_REL_F, bf16_store_tol(ro))
+    check("lse", host(lse), rlse, BF16_REL_F, BF16_MAX_ABS)
+    for name, a, ref in zip(("dk", "dv"), g32[1:], (rdk, rdv)):
+        check(name, host(a), ref, BF16_REL_F, BF16_MAX_ABS)
+    # dQ = scale sum_j dS_ij k_j takes dS rounded to bf16, and delta_i from
+    # the bf16-stored O, as any bf16 attention backward does.  Here the k_j
+    # share a large component along u and sum_j dS_ij = 0, so the sum cancels
+    # down to |dq| < 0.7 while its terms reach |dS| |k| ~ 10^2: those two
+    # roundings bound the error, not the size of dq.  First-order bound per
+    # element, with 2^-8 (twice the bf16 rounding) per rounded value:
+    #   scale 2^-8 (sum_j |dS_ij| |k_jc| + sum_c' |dO_ic' O_ic'| sum_j P_ij |k_jc|)
+    # (P, dS from the oracle's lse and O), plus the usual 2e-2.
+    gdq = host(g32[0])
+    scale = 1.0 / np.sqrt(d)
+    for h in range(Hq):
+        m = O.allowed_mask(L, G, O.head_shift(h, Hq, G, sh))
+        qh, kh, vh, dh = (x[0, :, h].astype(np.float64) for x in (q, k, v, do))
+        oh = ro[0, :, h]
+        P = np.where(m, np.exp(scale * qh @ kh.T - rlse[0, h][:, None]), 0.0)
+        dS = P * (dh @ vh.T - (dh * oh).sum(1)[:, None])
+        from_ds = np.abs(dS) @ np.abs(kh)
+        from_delta = np.abs(dh * oh).sum(1)[:, None] * (P @ np.abs(kh))
+        bound = scale * (from_ds + from_delta) * 2.0 ** -8 + BF16_MAX_ABS
+        err = np.abs(gdq[0, :, h] - rdq[0, :, h])
+        say(f"  dq[h{h}]    max_abs={err.max():.3e}, worst err/bound={float((err / bound).max()):.3f}")
+        assert (err <= bound).all(), f"dq of head {h} outside the bf16-dS rounding bound"
+
+
 # ---------------------------------------------------------------------------
 # The five workloads at full size.
 # ---------------------------------------------------------------------------
