@@ -359,6 +359,27 @@ def bench_block(args, wl):
     print(json.dumps(out), flush=True)
 
 
+def host_info():
+    """The host the CPU baseline ran on: CPU model, numpy and BLAS library."""
+    import platform
+
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    model = platform.processor() or ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = [f"{i.get('internal_api')} {i.get('version')}" for i in threadpool_info()
+            if i.get("user_api") == "blas"]
+    return {"cpu_model": model, "numpy": np.__version__, "blas": ", ".join(blas)}
+
+
 def cpu_baseline_block(wl, inp, seconds):
     """The block oracle (fp64 numpy) on the same workload: y at a few tokens at
     a time, each from the definition (every head's projections of the causal
@@ -391,7 +412,7 @@ def cpu_baseline_block(wl, inp, seconds):
     return {"value": round(fl / dt / 1e12, 5), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"block output y at {done} tokens of the same workload, fp64, each from its "
                       f"heads' causal group prefixes ({dt:.1f} s); forward only",
-            "seconds": round(dt, 2)}
+            "seconds": round(dt, 2), **host_info()}
 
 
 def cpu_baseline(wl, x, seconds):
@@ -420,7 +441,7 @@ def cpu_baseline(wl, x, seconds):
         return {"value": round(fl / dt / 1e12, 5), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
                 "sample": f"{done_rows} query rows drawn uniformly over the group, forward in fp64 row by row "
                           f"({dt:.1f} s); counted FLOPs 4*d per attended key",
-                "seconds": round(dt, 2)}
+                "seconds": round(dt, 2), **host_info()}
 
     scale = 1.0 / np.sqrt(wl.d)
     heads = [h for h in dict.fromkeys((0, wl.Hq - 1, wl.Hq // 2, 1, wl.Hq // 4, 3 * wl.Hq // 4, 2,
@@ -441,7 +462,7 @@ def cpu_baseline(wl, x, seconds):
     return {"value": round(fl / dt / 1e12, 5), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{done} (head, group) units of G={wl.G} rows, forward+backward in fp64 "
                       f"({dt:.1f} s); counted FLOPs as for the GPU",
-            "seconds": round(dt, 2)}
+            "seconds": round(dt, 2), **host_info()}
 
 
 if __name__ == "__main__":
