@@ -50,7 +50,7 @@ def kernel_source_sha():
 
 
 class ClockSampler:
-    """Samples the shader clock the driver reports (pp_dpm_sclk, the level
+    """Samples the shader clock the amdgpu kernel driver reports (pp_dpm_sclk, the level
     marked '*') every few milliseconds while the timed region runs."""
 
     def __init__(self, period_s=0.004):
@@ -118,7 +118,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(this build runs on a single GPU; units are independent, so several GPUs would "
+              "(the kernels run on one GPU; units are independent, so several GPUs would "
               "split heads or batch with no exchange)",
               file=sys.stderr)
         sys.exit(2)
