@@ -32,4 +32,4 @@ def test_host_info_names_cpu_numpy_and_blas():
 def test_kernel_source_hash_is_stable():
     b = _bench_module()
     h = b.kernel_source_sha()
-    assert h == b.kernel_source_sha() and len(h) == 64
+    assert h == b.kernel_source_sha() and len(h) == 16 and int(h, 16) >= 0
