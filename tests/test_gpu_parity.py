@@ -100,6 +100,29 @@ def test_small_f32_fwd_bwd(case):
         check(name, host(x), r, F32_TOL, F32_TOL)
 
 
+def test_many_small_units():
+    """L = 65536 cut into 1024 groups of 64: 4096 (head, group) units, one
+    query tile each, so the grid is tens of thousands of workgroups spread
+    over the XCDs by the unit map; whole tensors against the oracle.
+
+    With 4 M elements per gradient, the tail of the bf16 operand rounding
+    (P and dS enter the MFMAs as bf16) passes 2e-2 where |dk| nears 6, so
+    max-abs gets the bf16 rounding floor of the largest magnitude on top of
+    2e-2, as bf16-stored results do; rel_F keeps the usual 5e-3."""
+    B, L, Hq, Hkv, d, G, sh = 1, 65536, 4, 2, 64, 64, 2
+    say("[small units] L65536 G64")
+    q, k, v, do = rand_inputs(65, B, L, Hq, Hkv, d)
+    tq, tk, tv, tdo = (dev(x, BF) for x in (q, k, v, do))
+    o, lse = s2.forward(tq, tk, tv, G, sh)
+    g32 = s2.backward(tq, tk, tv, o, lse, tdo, G, sh, grad_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rdq, rdk, rdv, ro, rlse = O.backward(q, k, v, do, G, sh)
+    check("o", host(o), ro, BF16_REL_F, bf16_store_tol(ro))
+    check("lse", host(lse), rlse, BF16_REL_F, BF16_MAX_ABS)
+    for name, a, ref in zip(("dq", "dk", "dv"), g32, (rdq, rdk, rdv)):
+        check(name, host(a), ref, BF16_REL_F, bf16_store_tol(ref))
+
+
 def test_growing_scores_move_the_reference_max():
     """Scores that climb along the keys: q_i and k_j lie near one direction u,
     k_j scaled by its in-group position, so a row's running maximum rises by
