@@ -62,17 +62,43 @@ __global__ __launch_bounds__(FWD_THREADS) void fwd_bf16_kernel(Params p, int n_q
     constexpr int NSLOT = 2 * NCH / FWD_WAVES;  // 1 KB chunks per wave per tile; K first, then V
     const uint32_t rowb = (uint32_t)p.Hkv * D * 2;
     const size_t plane = ((size_t)w.b * p.L * p.Hkv + hk) * D;
-    ChunkSlot slot[NSLOT];
+    // K and V use the same chunks (j and j + NSLOT/2), so a wave holds
+    // NSLOT/2 slots.  A tile that neither wraps past the end of the sequence
+    // nor runs past the group is one run of rows starting at original row
+    // t0: its loads take a wave-uniform base and a fixed per-lane offset,
+    // with no per-load address arithmetic.
+    constexpr int NS2 = NSLOT / 2;
+    static_assert(NSLOT % 2 == 0 && (FWD_WAVES * NS2) % NCH == 0, "K and V share chunk slots");
+    ChunkSlot slot[NS2];
+    uint32_t lane_off[NS2];
 #pragma unroll
-    for (int j = 0; j < NSLOT; ++j) slot[j] = chunk_slot<D>((wave + FWD_WAVES * j) % NCH, lane);
+    for (int j = 0; j < NS2; ++j) {
+        slot[j] = chunk_slot<D>((wave + FWD_WAVES * j) % NCH, lane);
+        lane_off[j] = (uint32_t)slot[j].row * rowb + slot[j].colb;
+    }
     auto stage = [&](int kt, int buf) {
         char* base = smem + buf * 2 * TILE;
+        int t0 = w.g * p.G + s + kt * FWD_BN;  // original row of in-group index kt * FWD_BN
+        if (t0 >= p.L) t0 -= p.L;
+        const bool run = kt * FWD_BN + FWD_BN <= p.G && t0 + FWD_BN <= p.L;
+        if (run) {
+            const char* kb = reinterpret_cast<const char*>(k + plane) + (size_t)t0 * rowb;
+            const char* vb = reinterpret_cast<const char*>(v + plane) + (size_t)t0 * rowb;
 #pragma unroll
-        for (int j = 0; j < NSLOT; ++j) {
-            const bool isv = j >= NSLOT / 2;
-            const int cc = (wave + FWD_WAVES * j) % NCH;
-            const uint32_t off = row_off(w.g, p.G, kt * FWD_BN + slot[j].row, s, p.L, rowb) + slot[j].colb;
-            dma16((isv ? v : k) + plane, off, base + (isv ? TILE : 0) + cc * 1024);
+            for (int j = 0; j < NSLOT; ++j) {
+                const bool isv = j >= NS2;
+                const int cc = (wave + FWD_WAVES * j) % NCH;
+                dma16(isv ? vb : kb, lane_off[j % NS2], base + (isv ? TILE : 0) + cc * 1024);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < NSLOT; ++j) {
+                const bool isv = j >= NS2;
+                const int cc = (wave + FWD_WAVES * j) % NCH;
+                const ChunkSlot& sl = slot[j % NS2];
+                const uint32_t off = row_off(w.g, p.G, kt * FWD_BN + sl.row, s, p.L, rowb) + sl.colb;
+                dma16((isv ? v : k) + plane, off, base + (isv ? TILE : 0) + cc * 1024);
+            }
         }
     };
     stage(0, 0);
