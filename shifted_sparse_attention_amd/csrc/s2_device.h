@@ -116,9 +116,11 @@ __device__ __forceinline__ bf16x8 to_bf16x8(const float* x) {
 // barrier that hands the buffer to the readers.  Nothing else in these
 // kernels uses M0.
 // ---------------------------------------------------------------------------
+// The LDS address of a generic pointer into LDS is its low 32 bits (the
+// shared aperture is 4 GB aligned); truncating directly skips the null check
+// an address-space cast carries, which costs two scalar instructions per load.
 __device__ __forceinline__ uint32_t lds_addr(const char* lds) {
-    return __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)lds);
+    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
 }
 // gsrc = sbase + voff (voff a 32-bit byte offset, sbase wave-uniform).
 __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, char* lds_base) {
