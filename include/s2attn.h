@@ -26,9 +26,11 @@
  *     aligned.  Outputs must not alias inputs.  Outputs are overwritten, not
  *     accumulated into (dk, dv already hold the sum over the query heads that
  *     share a KV head).
- *   - Calls only enqueue work on `stream` (0 = the default stream).  The
- *     returned status covers argument checks and kernel launch; faults during
- *     execution surface at the caller's next synchronisation.
+ *   - Calls only enqueue kernel launches on `stream` (0 = the default
+ *     stream): no allocation, copy, memset or synchronisation, so they can be
+ *     captured in a HIP graph.  The returned status covers argument checks
+ *     and kernel launch; faults during execution surface at the caller's next
+ *     synchronisation.
  *   - Every argument check runs on the host before any HIP call, so invalid
  *     arguments are reported without touching the GPU.  Nothing is printed.
  *   - Stateless and thread-safe.
