@@ -79,8 +79,6 @@ int resolve_opts(const s2attn_opts* o, int d, Resolved* r) {
     return S2ATTN_OK;
 }
 
-size_t elem_size(int dtype) { return dtype == S2ATTN_F32 ? 4 : 2; }
-
 
 // Bytes of the dS tiles (blocks of 8 query rows, see Params::ds), in double so
 // the bound check cannot wrap for any accepted size.

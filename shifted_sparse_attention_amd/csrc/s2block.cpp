@@ -379,7 +379,6 @@ int s2block_bwd(const s2block_config* cfg, const void* x, const s2block_params* 
     Gemm g;
     TRY(setup(ws, ws_bytes, bw, stream, &g));
     char* base = static_cast<char*>(ws);
-    char* acat = base + bw.acat_off;
     char* t_o = base + bw.t_off;  // dy Bo
     char* dattn = base + bw.dattn_off;
     char* dqkv[3] = {base + bw.dq_off, base + bw.dk_off, base + bw.dv_off};
