@@ -358,6 +358,21 @@ def test_shift_counts_full_size(sh):
     _sampled_parity(wl2, x, outs, [(0, 5, 3), (0, 30, 0)], grads_f32=True)
 
 
+def test_d64_gqa_rope_full_size():
+    """d = 64 at a training length: L 32768, G 8192, 16 query / 4 KV heads
+    (8 shifted), RoPE-PI.  The d = 64 instantiations of every kernel (forward,
+    dK/dV with the dS tiles, dQ from them, the RoPE pre-pass and epilogues) at
+    full size: sampled units, one unshifted and the shifted last group that
+    wraps, and the group sums over every unit."""
+    wl = dataclasses.replace(CONFIGS["fwdbwd_bf16_L32k"], name="fwdbwd_bf16_L32k_d64_gqa_rope",
+                             Hq=16, Hkv=4, d=64, shifted_heads=8, seed=33, rope=True)
+    say(f"[d64] {wl.name}")
+    x = make_inputs(wl)
+    ins, outs = _run_fwdbwd(wl, x, grad_dtype=torch.float32)
+    _group_sums_hold(wl, ins[3], outs[3], outs[4], rope=True)
+    _sampled_parity(wl, x, outs, [(0, 0, 1), (0, 3, 3)], grads_f32=True)
+
+
 # ---------------------------------------------------------------------------
 # Kernel-level invariants.
 # ---------------------------------------------------------------------------
