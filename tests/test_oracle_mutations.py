@@ -17,6 +17,7 @@ from tests import test_oracle_pins as P
 def _pins(golden_dir):
     return [
         lambda: P.test_blog_shift_example(golden_dir),
+        lambda: P.test_brute_force_loops_on_the_blog_example(golden_dir),
         P.test_allowed_mask_structure,
         lambda: P.test_group_form_matches_explicit_mask(None),
         lambda: P.test_explicit_mask_matches_torch_sdpa_and_autograd(16, 4, 4, 4, 8, 2),

@@ -47,6 +47,51 @@ def test_blog_shift_example(golden_dir):
     assert O.head_shift(3, 4, G, 2) == s and O.head_shift(0, 4, G, 2) == 0
 
 
+def test_brute_force_loops_on_the_blog_example(golden_dir):
+    """Plain Python loops, no numpy algebra, on the blog's 12-token, 4-token
+    group example: each head's groups are read off the golden fixture (the
+    shifted head's as printed, with the cyclic reading of 13 and 14); query t
+    attends to the members of its group up to and including itself, in group
+    order.  O, LSE and all three gradients from those loops (dS = P (dP - D),
+    D = dO . O) must equal the oracle's group form."""
+    ex = json.load(open(os.path.join(golden_dir, "shift_example_blog_s33.json")))
+    L, G = ex["L"], ex["G"]
+    groups = {0: [[t - 1 for t in grp] for grp in ex["unshifted_groups_1based"]],
+              1: [[(t - 1) % L for t in grp] for grp in ex["shifted_groups_1based_as_printed"]]}
+    Hq, d = 2, 3
+    rng = np.random.default_rng(7)
+    q, k, v, do = (rng.standard_normal((1, L, Hq, d)) for _ in range(4))
+    scale = 1.0 / math.sqrt(d)
+    o = [[[0.0] * d for _ in range(Hq)] for _ in range(L)]
+    lse = [[0.0] * L for _ in range(Hq)]
+    dq, dk, dv = ([[[0.0] * d for _ in range(Hq)] for _ in range(L)] for _ in range(3))
+    for h in range(Hq):
+        for grp in groups[h]:
+            for a, t in enumerate(grp):
+                keys = grp[:a + 1]
+                sc = [scale * sum(q[0, t, h, c] * k[0, j, h, c] for c in range(d)) for j in keys]
+                mx = max(sc)
+                z = sum(math.exp(x - mx) for x in sc)
+                P = [math.exp(x - mx) / z for x in sc]
+                lse[h][t] = mx + math.log(z)
+                for c in range(d):
+                    o[t][h][c] = sum(P[n] * v[0, j, h, c] for n, j in enumerate(keys))
+                D = sum(do[0, t, h, c] * o[t][h][c] for c in range(d))
+                for n, j in enumerate(keys):
+                    dP = sum(do[0, t, h, c] * v[0, j, h, c] for c in range(d))
+                    dS = P[n] * (dP - D)
+                    for c in range(d):
+                        dq[t][h][c] += scale * dS * k[0, j, h, c]
+                        dk[j][h][c] += scale * dS * q[0, t, h, c]
+                        dv[j][h][c] += P[n] * do[0, t, h, c]
+    rdq, rdk, rdv, ro, rl = O.backward(q, k, v, do, G, 1)
+    np.testing.assert_allclose(ro[0], np.array(o), atol=1e-12)
+    np.testing.assert_allclose(rl[0], np.array(lse), atol=1e-12)
+    np.testing.assert_allclose(rdq[0], np.array(dq), atol=1e-12)
+    np.testing.assert_allclose(rdk[0], np.array(dk), atol=1e-12)
+    np.testing.assert_allclose(rdv[0], np.array(dv), atol=1e-12)
+
+
 def test_index_maps_inverse():
     for L, s in [(12, 2), (16, 4), (24, 3)]:
         t = np.arange(L)
