@@ -542,6 +542,37 @@ def test_backward_stages_equal_one_call(rope):
         assert torch.equal(a, b), name
 
 
+@pytest.mark.parametrize("rope", [None, (10000.0, 64)])
+def test_backward_stages_on_two_streams_without_ds(rope):
+    """Without dS tiles in the workspace (ds_max_mib = 0), DKDV and DQ read
+    only PRE's results and the inputs, so they may run concurrently: PRE on
+    one stream, then DKDV and DQ on two others that wait for it.  The
+    gradients equal one recomputing s2attn_bwd_ex call bit for bit."""
+    B, L, Hq, Hkv, d, G, sh = 1, 600, 4, 2, 128, 200, 2
+    say(f"[stages, two streams] rope={rope}")
+    q, k, v, do = rand_inputs(43, B, L, Hq, Hkv, d)
+    tq, tk, tv, tdo = (dev(x, BF) for x in (q, k, v, do))
+    o, lse = s2.forward(tq, tk, tv, G, sh, rope=rope)
+    ref = s2.backward(tq, tk, tv, o, lse, tdo, G, sh, rope=rope, ds_max_mib=0)
+    opts = s2.make_opts(BF, rope=rope, ds_max_mib=0)
+    n = s2.s2attn_workspace_size(1, B, L, Hq, Hkv, d, G, opts)
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dq, dk, dv = (torch.empty_like(x) for x in (tq, tk, tv))
+    torch.cuda.synchronize()
+    s_pre, s_kv, s_q = torch.cuda.Stream(), torch.cuda.Stream(), torch.cuda.Stream()
+    args = (tq, tk, tv, o, lse, tdo, dq, dk, dv, B, L, Hq, Hkv, d, G, sh, opts, ws, n)
+    s2.s2attn_bwd_stage_ex(s2.S2ATTN_BWD_STAGE_PRE, *args, stream=s_pre)
+    done = torch.cuda.Event()
+    done.record(s_pre)
+    s_kv.wait_event(done)
+    s_q.wait_event(done)
+    s2.s2attn_bwd_stage_ex(s2.S2ATTN_BWD_STAGE_DKDV, *args, stream=s_kv)
+    s2.s2attn_bwd_stage_ex(s2.S2ATTN_BWD_STAGE_DQ, *args, stream=s_q)
+    torch.cuda.synchronize()
+    for name, a, want in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
+        assert torch.equal(a, want), name
+
+
 def test_graph_capture_replays_bitwise():
     """The forward and backward enqueue only kernel launches on the caller's
     stream (no allocation, copy, memset or synchronisation), so a caller can
