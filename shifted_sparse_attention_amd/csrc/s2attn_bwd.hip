@@ -400,6 +400,19 @@ __global__ __launch_bounds__(64 * DKV_WAVES) void bwd_dkdv_bf16_kernel(Params p,
             sacc = mfma32(ld_lds16(sQ, off), kf, sacc);
             pacc = mfma32(ld_lds16(sO, off), ld_lds16(sVt, koff), pacc);
         }
+        // LDS operand reads run 8 ahead of the MFMAs that use them, then two
+        // per MFMA: the default schedule kept them one or two ahead, so each
+        // MFMA waited on its own operands (5% of the kernel).
+        {
+            constexpr int NR = 4 * KS - KREG, NM = 2 * KS, AHEAD = 8, PAIRS = (NR - AHEAD) / 2;
+            __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
+#pragma unroll
+            for (int i = 0; i < PAIRS; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, NM - PAIRS, 0);
+        }
         // P and dS; element i is query qb + 8(i/4) + 4hh + i%4 and key kj.
         auto softmax_grad = [&](bool mask) {
 #pragma unroll
@@ -457,6 +470,17 @@ __global__ __launch_bounds__(64 * DKV_WAVES) void bwd_dkdv_bf16_kernel(Params p,
                                       ld_lds_tr(sQ, tile_off<D>(row + 8, col)));
                 dk[cb] = mfma32(qq, db[kk], dk[cb]);
             }
+        }
+        // Transposed reads 12 ahead, then two per MFMA.
+        {
+            constexpr int NR = 8 * CB, NM = 4 * CB, AHEAD = 12, PAIRS = (NR - AHEAD) / 2;
+            __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
+#pragma unroll
+            for (int i = 0; i < PAIRS; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, NM - PAIRS, 0);
         }
     }
 
