@@ -608,6 +608,17 @@ __global__ __launch_bounds__(64 * DQ_WAVES) void bwd_dq_bf16_kernel(Params p, in
                 pacc[mb] = mfma32(ld_lds16(sV, off), gf[ks], pacc[mb]);
             }
         }
+        // K and V operand reads run 6 ahead of their MFMAs (then one per MFMA).
+        {
+            constexpr int NR = 4 * KS, NM = 4 * KS, AHEAD = 6;
+            __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
+#pragma unroll
+            for (int i = 0; i < NR - AHEAD; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, NM - (NR - AHEAD), 0);
+        }
         auto softmax_grad = [&](bool mask) {
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
@@ -643,6 +654,17 @@ __global__ __launch_bounds__(64 * DQ_WAVES) void bwd_dq_bf16_kernel(Params p, in
                                        ld_lds_tr(sK, tile_off<D>(row + 8, col)));
                 dq[cb] = mfma32(kt_, db[kk], dq[cb]);
             }
+        }
+        // Transposed K reads 8 ahead (then two per MFMA).
+        {
+            constexpr int NR = 8 * CB, NM = 4 * CB, AHEAD = 8, PAIRS = (NR - AHEAD) / 2;
+            __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
+#pragma unroll
+            for (int i = 0; i < PAIRS; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, NM - PAIRS, 0);
         }
     }
 
