@@ -119,9 +119,10 @@ int s2attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  * Backward, bf16 inputs and gradients, scale 1/sqrt(d), no RoPE.
  * Reads q, k, v, o, lse (as written by s2attn_fwd on the same inputs) and
  * dout; writes dq, dk, dv.  delta_ws is caller scratch of 2*B*Hq*L floats
- * (receives -rowsum(dout * o) and lse * log2(e), each [B, Hq, L]).  Gradient formulas: with P the attention
- * probabilities, dS = P * (dout . v_j - delta), dq = scale dS k,
- * dk = scale dS^T q, dv = P^T dout (summed over query heads per KV head).
+ * (receives -rowsum(dout * o) and lse * log2(e), each [B, Hq, L]).
+ * Gradient formulas: with P the attention probabilities,
+ * dS = P * (dout . v_j - delta), dq = scale dS k, dk = scale dS^T q,
+ * dv = P^T dout (summed over query heads per KV head).
  */
 int s2attn_bwd(const void* q, const void* k, const void* v, const void* o,
                const float* lse, const void* dout, void* dq, void* dk, void* dv,
@@ -169,8 +170,9 @@ int s2attn_bwd_ex(const void* q, const void* k, const void* v, const void* o,
  *   S2ATTN_BWD_STAGE_DQ    dq.  Needs PRE complete, and DKDV complete when the
  *                          workspace holds dS tiles (see s2attn_workspace_size).
  * PRE, DKDV, DQ in that order on one stream equal s2attn_bwd_ex.  Without dS
- * tiles (fp32, or groups too large) DKDV and DQ read only PRE's results and
- * the inputs and may run concurrently on two streams once PRE has finished.
+ * tiles (fp32 inputs, or a dS region above opts->ds_max_mib) DKDV and DQ read
+ * only PRE's results and the inputs and may run concurrently on two streams
+ * once PRE has finished.
  * Any other stage value: S2ATTN_ERR_INVALID_ARG.
  */
 int s2attn_bwd_stage_ex(int stage, const void* q, const void* k, const void* v, const void* o,

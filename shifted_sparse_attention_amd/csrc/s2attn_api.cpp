@@ -79,7 +79,6 @@ int resolve_opts(const s2attn_opts* o, int d, Resolved* r) {
     return S2ATTN_OK;
 }
 
-
 // Bytes of the dS tiles (blocks of 8 query rows, see Params::ds), in double so
 // the bound check cannot wrap for any accepted size.
 double ds_bytes_f(int B, int Hq, int L, int G) {
