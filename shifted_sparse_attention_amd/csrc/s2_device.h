@@ -15,7 +15,6 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -53,12 +52,9 @@ __device__ __forceinline__ int tile_off(int row, int col) {
     return row * (D * 2) + slot * 16 + (col & 7) * 2;
 }
 
-// 16-byte global load / LDS store / LDS load.
+// 16-byte global load / LDS load.
 __device__ __forceinline__ u32x4 ld_global16(const void* p) {
     return *reinterpret_cast<const u32x4*>(p);
-}
-__device__ __forceinline__ void st_lds16(char* lds, int off, u32x4 v) {
-    *reinterpret_cast<u32x4*>(lds + off) = v;
 }
 __device__ __forceinline__ bf16x8 ld_lds16(const char* lds, int off) {
     return *reinterpret_cast<const bf16x8*>(lds + off);

@@ -28,7 +28,7 @@ struct Params {
     // in blocks of 8 (t = q32 / 8), each block stored k32-major over its
     // 8 (t + 1) key tiles: tile (q32, k32) is number 32 t (t + 1) + 8 k32 +
     // q32 % 8 of the unit, whose UT = 32 NB (NB + 1) tiles (NB = ceil(T / 8))
-    // start at tile (b Hq + h) n_g + g) * UT.  So the 8 rows one dQ
+    // start at tile ((b Hq + h) n_g + g) UT.  So the 8 rows one dQ
     // workgroup reads advance through consecutive memory.  Within a tile,
     // the four bf16 of key r (0..31) and query quad c (queries 4c .. 4c+3)
     // sit at byte 1024 (c >> 2) + 16 (r + 32 (c & 1)) + 8 ((c >> 1) & 1): the

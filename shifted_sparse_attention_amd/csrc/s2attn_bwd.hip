@@ -693,16 +693,16 @@ __global__ __launch_bounds__(64 * DQ_WAVES) void bwd_dq_bf16_kernel(Params p, in
 // ---------------------------------------------------------------------------
 constexpr int DQS_WAVES = 8;
 constexpr int DQS_BQ = 32 * DQS_WAVES;
-// Keys per stage and stages in LDS; NBUF - 1 stages are in flight while one
-// is consumed.
-template <int D> constexpr int dqs_bk() { return 64; }
-template <int D> constexpr int dqs_nbuf() { return 3; }
+// Keys per stage and stages in LDS; DQS_NBUF - 1 stages are in flight while
+// one is consumed.
+constexpr int DQS_BK = 64;
+constexpr int DQS_NBUF = 3;
 
 template <int D, bool GRAD_F32>
 __global__ __launch_bounds__(64 * DQS_WAVES) void bwd_dq_ds_kernel(Params p, int n_qt) {
     constexpr int CB = D / 32;
-    constexpr int BK = dqs_bk<D>();
-    constexpr int NBUF = dqs_nbuf<D>();
+    constexpr int BK = DQS_BK;
+    constexpr int NBUF = DQS_NBUF;
     constexpr int KT32 = BK / 32;              // dS tiles per wave per stage
     constexpr int KTILE = BK * D * 2;          // one K tile
     constexpr int KNCH = KTILE / 1024;

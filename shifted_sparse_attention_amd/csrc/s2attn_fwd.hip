@@ -13,9 +13,10 @@
 namespace s2 {
 
 // ---------------------------------------------------------------------------
-// bf16 forward.  8 waves x 32 queries per workgroup; K and V tiles of 64 keys
-// are staged in LDS by direct global->LDS loads into two buffers, so the next
-// tile streams in while the current one is consumed (one barrier per tile).
+// bf16 forward.  8 waves x 32 queries per workgroup; K and V tiles of 128
+// keys are staged in LDS by direct global->LDS loads into two buffers, so the
+// next tile streams in while the current one is consumed (one barrier per
+// tile).
 // Scores are formed transposed, S^T = K Q^T, so a lane owns one query column
 // and 16 of the 32 keys of each 32-key block (the other 16 sit in lane ^ 32):
 // the row max needs one permlane32 swap, the row sum none until the end.
