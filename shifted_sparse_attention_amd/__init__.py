@@ -15,8 +15,9 @@ import torch
 
 from . import flops  # noqa: F401
 from ._lib import (  # noqa: F401
-    LIB_PATH, S2ATTN_BF16, S2ATTN_BWD_STAGE_DKDV, S2ATTN_BWD_STAGE_DQ, S2ATTN_BWD_STAGE_PRE, S2ATTN_ERR_HIP, S2ATTN_ERR_INVALID_ARG, S2ATTN_ERR_UNSUPPORTED,
-    S2ATTN_ERR_WORKSPACE, S2ATTN_F32, S2ATTN_OK, S2AttnError, lib, s2attn_bwd, s2attn_bwd_ex, s2attn_bwd_stage_ex,
+    LIB_PATH, S2ATTN_BF16, S2ATTN_BWD_STAGE_DKDV, S2ATTN_BWD_STAGE_DQ, S2ATTN_BWD_STAGE_PRE,
+    S2ATTN_ERR_HIP, S2ATTN_ERR_INVALID_ARG, S2ATTN_ERR_UNSUPPORTED, S2ATTN_ERR_WORKSPACE,
+    S2ATTN_F32, S2ATTN_OK, S2AttnError, lib, s2attn_bwd, s2attn_bwd_ex, s2attn_bwd_stage_ex,
     s2attn_fwd, s2attn_fwd_ex, s2attn_opts, s2attn_opts_init, s2attn_status_string,
     s2attn_version, s2attn_workspace_size, s2block_bwd, s2block_config, s2block_config_init,
     s2block_fwd, s2block_grads, s2block_params, s2block_saved, s2block_workspace_size)
@@ -41,9 +42,12 @@ def make_opts(dtype, grad_dtype=None, scale=None, rope=None, ds_max_mib=None):
     """Build s2attn_opts.  `rope` is None or (base, orig_len); `ds_max_mib`
     bounds the dS tiles the backward keeps in its workspace (None: the
     library default, 0: never)."""
+    gd = grad_dtype if grad_dtype is not None else dtype
+    if dtype not in _DT or gd not in _DT:
+        raise ValueError("dtypes must be torch.bfloat16 or torch.float32")
     o = s2attn_opts_init()
     o.dtype = _DT[dtype]
-    o.grad_dtype = _DT[grad_dtype if grad_dtype is not None else dtype]
+    o.grad_dtype = _DT[gd]
     o.softmax_scale = 0.0 if scale is None else float(scale)
     if rope is not None:
         o.rope = 1
@@ -61,7 +65,7 @@ def forward(q, k, v, G, shifted_heads, *, scale=None, rope=None, stream=None):
     lse = torch.empty((B, Hq, L), dtype=torch.float32, device=q.device)
     opts = make_opts(q.dtype, scale=scale, rope=rope)
     ws_bytes = s2attn_workspace_size(0, B, L, Hq, Hkv, d, G, opts)
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device) if ws_bytes else None
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
     s2attn_fwd_ex(q, k, v, o, lse, B, L, Hq, Hkv, d, G, shifted_heads, opts, ws, ws_bytes, stream)
     return o, lse
 
