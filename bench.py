@@ -111,6 +111,9 @@ def parse():
                          "value and ms_per_step then come from the per-step spans, which exclude the flush")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="after timing, run one device copy of this many MiB (counter calibration)")
+    ap.add_argument("--two-step-sdpa", action="store_true",
+                    help="also time the method in its two-step PyTorch form (torch.roll, groups folded "
+                         "into the batch, torch SDPA's flash kernel) on the same inputs, as context")
     return ap.parse_args()
 
 
@@ -261,9 +264,113 @@ def main():
         "cus": torch.cuda.get_device_properties(dev).multi_processor_count,
     }
 
+    if args.two_step_sdpa:
+        out["two_step_sdpa"] = time_two_step_sdpa(wl, tq, tk, tv, tdo, (o, dq, dk, dv), args.steps,
+                                                  args.warmup, fl)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def _roll_heads(x, shifted_heads, shift):
+    """The last `shifted_heads` heads of x [B, L, H, d] rolled by `shift` along L (a copy)."""
+    import torch
+    if shifted_heads == 0:
+        return x
+    H = x.shape[2]
+    return torch.cat([x[:, :, :H - shifted_heads], x[:, :, H - shifted_heads:].roll(shift, dims=1)], dim=2)
+
+
+def _fold(x, G, shifted_heads):
+    """[B, L, H, d] -> [B * L / G, H, G, d]: shifted heads rolled by -G/2, groups folded into
+    the batch (a strided view of the rolled tensor)."""
+    B, L, H, d = x.shape
+    return _roll_heads(x, shifted_heads, -(G // 2)).reshape(B * (L // G), G, H, d).transpose(1, 2)
+
+
+def _unfold(y, L, G, shifted_heads):
+    """Inverse of _fold."""
+    N, H, _, d = y.shape
+    return _roll_heads(y.transpose(1, 2).reshape(N * G // L, L, H, d), shifted_heads, G // 2)
+
+
+def two_step_form(q, k, v, G, shifted_heads):
+    """S2-Attn the way the LongLoRA pages implement it in PyTorch (blog section 3.3;
+    nearauto.com article, shift-short-attention section): the last `shifted_heads` heads
+    are rolled by -G/2 along the sequence (torch.roll, a copy), the groups are folded into
+    the batch (a view), causal attention runs per group (torch's scaled_dot_product_attention,
+    whichever backend the caller enables), and the output is unfolded and rolled back.
+    q, k, v: [B, L, H, d] with one KV head per query head.  Differentiable through autograd."""
+    import torch.nn.functional as Fn
+    y = Fn.scaled_dot_product_attention(_fold(q, G, shifted_heads), _fold(k, G, shifted_heads),
+                                        _fold(v, G, shifted_heads), is_causal=True)
+    return _unfold(y, q.shape[1], G, shifted_heads)
+
+
+def time_two_step_sdpa(wl, tq, tk, tv, tdo, ours, steps, warmup, counted_flops):
+    """two_step_form on this GPU (forward, and backward for fwd+bwd workloads) with torch SDPA
+    restricted to its flash kernel (no fallback to the math path), timed like the main steps;
+    outputs compared with this library's (`ours` = o, dq, dk, dv of the same inputs).
+    Context, not a target: it measures torch's kernels and copies."""
+    import torch
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    if wl.Hq != wl.Hkv or wl.rope:
+        return {"skipped": "multi-head workloads without RoPE only"}
+    q, k, v = (t.detach().clone().requires_grad_(wl.backward) for t in (tq, tk, tv))
+
+    def step():
+        q.grad = k.grad = v.grad = None
+        with sdpa_kernel([SDPBackend.FLASH_ATTENTION]), torch.set_grad_enabled(wl.backward):
+            y = two_step_form(q, k, v, wl.G, wl.shifted_heads)
+            if wl.backward:
+                y.backward(tdo)
+        return y
+
+    try:
+        y = step()
+    except RuntimeError as e:   # no flash kernel for this shape or device
+        return {"skipped": f"torch SDPA flash kernel unavailable: {str(e).splitlines()[0][:200]}"}
+    torch.cuda.synchronize()
+
+    def rel_f(a, b):
+        a, b = a.double(), b.double()
+        return float(torch.linalg.vector_norm(a - b) / torch.linalg.vector_norm(b))
+
+    got = (y.detach(), q.grad, k.grad, v.grad) if wl.backward else (y,)
+    agree = {n: round(rel_f(a, b), 6) for n, a, b in zip(("o", "dq", "dk", "dv"), got, ours)}
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for _ in range(steps):
+            fn()
+        end.record(stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / steps
+
+    ms = timed(step)
+    # The attention kernels alone: inputs already rolled and folded into contiguous
+    # [B * L / G, H, G, d] tensors, so no roll or layout copy is timed.
+    qf, kf, vf = (_fold(t, wl.G, wl.shifted_heads).contiguous().requires_grad_(wl.backward)
+                  for t in (tq, tk, tv))
+    dof = _fold(tdo, wl.G, wl.shifted_heads).contiguous() if wl.backward else None
+
+    def step_attention():
+        qf.grad = kf.grad = vf.grad = None
+        with sdpa_kernel([SDPBackend.FLASH_ATTENTION]), torch.set_grad_enabled(wl.backward):
+            yf = torch.nn.functional.scaled_dot_product_attention(qf, kf, vf, is_causal=True)
+            if wl.backward:
+                yf.backward(dof)
+
+    ms_attn = timed(step_attention)
+    return {"ms_per_step": round(ms, 4), "tflops": round(counted_flops / (ms * 1e-3) / 1e12, 2),
+            "attention_only_ms": round(ms_attn, 4),
+            "attention_only_tflops": round(counted_flops / (ms_attn * 1e-3) / 1e12, 2),
+            "backend": "torch SDPA, flash kernel only (AOTriton on ROCm)",
+            "rel_frobenius_vs_libs2attn": agree, "torch": torch.__version__}
 
 
 def bench_block(args, wl):

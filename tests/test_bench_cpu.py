@@ -33,3 +33,27 @@ def test_kernel_source_hash_is_stable():
     b = _bench_module()
     h = b.kernel_source_sha()
     assert h == b.kernel_source_sha() and len(h) == 16 and int(h, 16) >= 0
+
+
+def test_two_step_form_is_s2attn():
+    """bench.py's two-step PyTorch form (roll, fold groups into the batch, causal SDPA,
+    unfold, roll back) computes S2-Attn: fp64 on the CPU it equals the oracle's group form,
+    outputs and gradients, with no, some and all heads shifted."""
+    import numpy as np
+    import torch
+
+    sys.path.insert(0, ROOT)
+    from oracle import s2attn as ref
+
+    two_step_form = _bench_module().two_step_form
+    rng = np.random.default_rng(7)
+    B, L, H, d, G = 2, 24, 4, 8, 6
+    q, k, v, do = (rng.standard_normal((B, L, H, d)) for _ in range(4))
+    for sh in (0, 2, 4):
+        tq, tk, tv = (torch.tensor(a, requires_grad=True) for a in (q, k, v))
+        y = two_step_form(tq, tk, tv, G, sh)
+        y.backward(torch.tensor(do))
+        o, _ = ref.forward(q, k, v, G, sh)
+        dq, dk, dv, _, _ = ref.backward(q, k, v, do, G, sh)
+        for got, want in ((y.detach(), o), (tq.grad, dq), (tk.grad, dk), (tv.grad, dv)):
+            np.testing.assert_allclose(got.numpy(), want, rtol=0, atol=1e-12)
