@@ -172,18 +172,29 @@ __device__ __forceinline__ uint32_t row_off(int g, int G, int jg, int s, int L, 
 // Work decode shared by the tiled kernels: unit (b, h, g) and tile index
 // from the flat block id.  Workgroups are dispatched round-robin over the 8
 // XCDs; when the unit count is a multiple of 8, every tile of a unit lands
-// on the same XCD (so its K/V stay in that XCD's L2), and tiles of a unit
-// are issued longest-first.
+// on the same XCD (so the data its workgroups re-read stays in that XCD's
+// L2 or the last-level cache).  Each XCD takes its units in bands of `band`
+// units (dispatch_band; the last band may be smaller).  Inside a band the
+// tiles go longest first across the band's units, tile-major.  Bands of
+// several units keep the longest tiles of an XCD's last units from starting
+// last when units have few tiles (small groups) and spread the memory
+// stream over more units.  Band 1 is unit by unit, each unit's tiles
+// longest first.
 struct Work {
     int b, h, g, tile;
 };
 
-__device__ __forceinline__ Work decode_work(int bid, int n_units, int n_tiles, int Hh, int n_g) {
+__device__ __forceinline__ Work decode_work(int bid, int n_units, int n_tiles, int Hh, int n_g,
+                                            int band) {
     int u, t;
     if ((n_units & 7) == 0) {
-        int xcd = bid & 7, slot = bid >> 3;
-        u = (slot / n_tiles) * 8 + xcd;
-        t = slot % n_tiles;
+        const int xcd = bid & 7, slot = bid >> 3;
+        const int upx = n_units >> 3;                          // units per XCD
+        const int first = slot / (band * n_tiles) * band;      // the band's first unit on the XCD
+        const int nb = min(band, upx - first);                 // units in the band
+        const int r = slot - first * n_tiles;                  // position inside the band
+        t = r / nb;
+        u = (first + r % nb) * 8 + xcd;
     } else {
         u = bid / n_tiles;
         t = bid % n_tiles;

@@ -45,7 +45,23 @@ struct Params {
     // (divided by 2 pi), formed in double precision on the host.
     int rope;
     double rope_rev[64];
+    // Units per dispatch band of the tiled kernels (see decode_work; >= 1).
+    int band;
 };
+
+// Dispatch band for a kernel whose workgroups of one unit re-read
+// `reuse_bytes` (K and V, K alone, or Q and dO): as many units as keep the
+// bands of the 8 XCDs within the 256 MB last-level cache (32 MiB per XCD),
+// at least 1 and at most the units of one XCD.  Measured at 8k-100k tokens,
+// wider bands than that lose (more misses), narrower ones leave the tail of
+// few-tile units and a less even memory stream.
+inline int dispatch_band(int n_units, size_t reuse_bytes) {
+    const size_t budget = (size_t)32 << 20;
+    const size_t upx = (size_t)(n_units / 8);
+    size_t band = reuse_bytes > 0 ? budget / reuse_bytes : 1;
+    if (band > upx) band = upx;
+    return band < 1 ? 1 : (int)band;
+}
 
 // Head shift: half a group for the last `shifted_heads` query heads.
 __host__ __device__ inline int head_shift(const Params& p, int h) {

@@ -149,6 +149,7 @@ s2::Params make_params(int B, int L, int Hq, int Hkv, int d, int G, int shifted_
     p.n_g = L / G;
     p.scale = r.scale;
     p.scale_log2 = r.scale * 1.4426950408889634f;
+    p.band = 1;
     p.rope = r.rope;
     if (r.rope) {
         // LongLoRA blog, section 3.4: positions [0, L) are squeezed onto [0, L0).

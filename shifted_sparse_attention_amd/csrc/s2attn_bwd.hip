@@ -265,7 +265,7 @@ __global__ __launch_bounds__(64 * DKV_WAVES) void bwd_dkdv_bf16_kernel(Params p,
     char* bufs = smem + 2 * KTILE;
 
     const int n_units = p.B * p.Hkv * p.n_g;
-    Work w = decode_work(blockIdx.x, n_units, n_kt, p.Hkv, p.n_g);
+    Work w = decode_work(blockIdx.x, n_units, n_kt, p.Hkv, p.n_g, p.band);
     w.tile = n_kt - 1 - w.tile;  // key tile 0 has the most queries: issue it first
     const int hk = w.h;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -527,7 +527,7 @@ __global__ __launch_bounds__(64 * DQ_WAVES) void bwd_dq_bf16_kernel(Params p, in
     __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * TILE];
 
     const int n_units = p.B * p.Hq * p.n_g;
-    const Work w = decode_work(blockIdx.x, n_units, n_qt, p.Hq, p.n_g);
+    const Work w = decode_work(blockIdx.x, n_units, n_qt, p.Hq, p.n_g, p.band);
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hh = lane >> 5, l32 = lane & 31;
@@ -713,7 +713,7 @@ __global__ __launch_bounds__(64 * DQS_WAVES) void bwd_dq_ds_kernel(Params p, int
     __shared__ __attribute__((aligned(1024))) char smem[NBUF * STAGE];
 
     const int n_units = p.B * p.Hq * p.n_g;
-    const Work w = decode_work(blockIdx.x, n_units, n_qt, p.Hq, p.n_g);
+    const Work w = decode_work(blockIdx.x, n_units, n_qt, p.Hq, p.n_g, p.band);
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hh = lane >> 5;
@@ -836,7 +836,7 @@ __global__ __launch_bounds__(F32_ROWS) void bwd_dq_f32_kernel(Params p, int n_qt
     __shared__ float sK[F32_ROWS][D];
     __shared__ float sV[F32_ROWS][D];
     const int n_units = p.B * p.Hq * p.n_g;
-    const Work w = decode_work(blockIdx.x, n_units, n_qt, p.Hq, p.n_g);
+    const Work w = decode_work(blockIdx.x, n_units, n_qt, p.Hq, p.n_g, p.band);
     const int tid = threadIdx.x;
     const int s = head_shift(p, w.h);
     const int hk = w.h / p.r;
@@ -899,7 +899,7 @@ __global__ __launch_bounds__(F32_ROWS) void bwd_dkdv_f32_kernel(Params p, int n_
     __shared__ float sG[F32_ROWS][D];
     __shared__ float sL[F32_ROWS], sD[F32_ROWS];
     const int n_units = p.B * p.Hkv * p.n_g;
-    Work w = decode_work(blockIdx.x, n_units, n_kt, p.Hkv, p.n_g);
+    Work w = decode_work(blockIdx.x, n_units, n_kt, p.Hkv, p.n_g, p.band);
     w.tile = n_kt - 1 - w.tile;
     const int hk = w.h;
     const int tid = threadIdx.x;
@@ -1008,17 +1008,21 @@ hipError_t launch_rope_prepass(const Params& p, void* q_out, void* k_out, hipStr
 }
 
 template <int D, bool GF>
-static void launch_dkdv_t(const Params& p, hipStream_t st) {
-    const int n_kt = (p.G + DKV_BK - 1) / DKV_BK;
-    const long blocks = (long)p.B * p.Hkv * p.n_g * n_kt;
+static void launch_dkdv_t(const Params& p0, hipStream_t st) {
+    const int n_kt = (p0.G + DKV_BK - 1) / DKV_BK;
+    const long blocks = (long)p0.B * p0.Hkv * p0.n_g * n_kt;
+    Params p = p0;  // band: Q and dO of the r query heads of the unit
+    p.band = dispatch_band(p.B * p.Hkv * p.n_g, (size_t)p.r * p.G * p.d * 4);
     hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, GF>), dim3(blocks), dim3(64 * DKV_WAVES), 0, st, p,
                        n_kt);
 }
 
 template <int D, bool GF>
-static void launch_dq_t(const Params& p, hipStream_t st) {
-    const int n_qt = (p.G + DQ_BQ - 1) / DQ_BQ;
-    const long blocks = (long)p.B * p.Hq * p.n_g * n_qt;
+static void launch_dq_t(const Params& p0, hipStream_t st) {
+    const int n_qt = (p0.G + DQ_BQ - 1) / DQ_BQ;
+    const long blocks = (long)p0.B * p0.Hq * p0.n_g * n_qt;
+    Params p = p0;  // band: K and V of the unit
+    p.band = dispatch_band(p.B * p.Hq * p.n_g, (size_t)p.G * p.d * 4);
     hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, GF>), dim3(blocks), dim3(64 * DQ_WAVES), 0, st, p,
                        n_qt);
 }
@@ -1032,9 +1036,11 @@ hipError_t launch_bwd_dkdv_bf16(const Params& p, int grad_f32, hipStream_t st) {
 }
 
 template <int D, bool GF>
-static void launch_dq_ds_t(const Params& p, hipStream_t st) {
-    const int n_qt = (p.G + DQS_BQ - 1) / DQS_BQ;
-    const long blocks = (long)p.B * p.Hq * p.n_g * n_qt;
+static void launch_dq_ds_t(const Params& p0, hipStream_t st) {
+    const int n_qt = (p0.G + DQS_BQ - 1) / DQS_BQ;
+    const long blocks = (long)p0.B * p0.Hq * p0.n_g * n_qt;
+    Params p = p0;  // band: K of the unit (the dS tiles stream through once)
+    p.band = dispatch_band(p.B * p.Hq * p.n_g, (size_t)p.G * p.d * 2);
     hipLaunchKernelGGL((bwd_dq_ds_kernel<D, GF>), dim3(blocks), dim3(64 * DQS_WAVES), 0, st, p,
                        n_qt);
 }

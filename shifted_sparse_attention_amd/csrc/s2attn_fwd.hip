@@ -40,7 +40,7 @@ __global__ __launch_bounds__(FWD_THREADS) void fwd_bf16_kernel(Params p, int n_q
     __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * TILE];
 
     const int n_units = p.B * p.Hq * p.n_g;
-    const Work w = decode_work(blockIdx.x, n_units, n_qt, p.Hq, p.n_g);
+    const Work w = decode_work(blockIdx.x, n_units, n_qt, p.Hq, p.n_g, p.band);
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hh = lane >> 5, l32 = lane & 31;
@@ -261,7 +261,7 @@ __global__ __launch_bounds__(F32_ROWS) void fwd_f32_kernel(Params p, int n_qt) {
     __shared__ float sK[F32_ROWS][D];
     __shared__ float sV[F32_ROWS][D];
     const int n_units = p.B * p.Hq * p.n_g;
-    const Work w = decode_work(blockIdx.x, n_units, n_qt, p.Hq, p.n_g);
+    const Work w = decode_work(blockIdx.x, n_units, n_qt, p.Hq, p.n_g, p.band);
     const int tid = threadIdx.x;
     const int s = head_shift(p, w.h);
     const int hk = w.h / p.r;
@@ -327,9 +327,11 @@ __global__ __launch_bounds__(F32_ROWS) void fwd_f32_kernel(Params p, int n_qt) {
 // ---------------------------------------------------------------------------
 // Launchers.
 // ---------------------------------------------------------------------------
-hipError_t launch_fwd_bf16(const Params& p, hipStream_t st) {
-    const int n_qt = (p.G + FWD_BM - 1) / FWD_BM;
-    const long blocks = (long)p.B * p.Hq * p.n_g * n_qt;
+hipError_t launch_fwd_bf16(const Params& p0, hipStream_t st) {
+    const int n_qt = (p0.G + FWD_BM - 1) / FWD_BM;
+    const long blocks = (long)p0.B * p0.Hq * p0.n_g * n_qt;
+    Params p = p0;
+    p.band = dispatch_band(p.B * p.Hq * p.n_g, (size_t)p.G * p.d * 4);  // K and V of the unit
     if (p.d == 128)
         hipLaunchKernelGGL(fwd_bf16_kernel<128>, dim3(blocks), dim3(FWD_THREADS), 0, st, p, n_qt);
     else

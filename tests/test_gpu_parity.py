@@ -373,6 +373,52 @@ def test_d64_gqa_rope_full_size():
     _sampled_parity(wl, x, outs, [(0, 0, 1), (0, 3, 3)], grads_f32=True)
 
 
+def test_dispatch_bands_with_a_partial_last_band():
+    """40 (head, group) units of one 32768-token group each at d = 64: 5 units
+    per XCD.  The forward, dK/dV and the recomputing dQ re-read 8 MiB per unit,
+    so they dispatch in bands of 4 units and the last band holds one; dQ from
+    the stored dS re-reads 4 MiB and takes all 5 in one band.  Every output is
+    written (NaN-filled buffers come back finite), sampled rows of heads in
+    both bands match the oracle, the group sums hold over every unit, dK and
+    dV agree bitwise with and without stored dS, and the two dQ agree."""
+    B, L, Hq, Hkv, d, G, sh = 1, 32768, 40, 40, 64, 32768, 20
+    say("[bands] L32768 G32768 H40 d64")
+    q, k, v, do = rand_inputs(4040, B, L, Hq, Hkv, d)
+    tq, tk, tv, tdo = (dev(x, BF) for x in (q, k, v, do))
+
+    def nan(shape, dtype):
+        return torch.full(shape, float("nan"), dtype=dtype, device="cuda")
+
+    o, lse = nan(tq.shape, BF), nan((B, Hq, L), torch.float32)
+    s2.s2attn_fwd_ex(tq, tk, tv, o, lse, B, L, Hq, Hkv, d, G, sh, s2.make_opts(BF), None, 0)
+    grads = {}
+    for ds_max in (None, 0):   # dS tiles kept (43 GB), then not kept
+        opts = s2.make_opts(BF, grad_dtype=torch.float32, ds_max_mib=ds_max)
+        wsb = s2.s2attn_workspace_size(1, B, L, Hq, Hkv, d, G, opts)
+        assert (wsb > 40e9) == (ds_max is None)
+        ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+        g = tuple(nan(t.shape, torch.float32) for t in (tq, tk, tv))
+        s2.s2attn_bwd_ex(tq, tk, tv, o, lse, tdo, *g, B, L, Hq, Hkv, d, G, sh, opts, ws, wsb)
+        torch.cuda.synchronize()
+        del ws
+        grads[ds_max] = g
+    for t in (o, lse) + grads[None] + grads[0]:
+        assert bool(torch.isfinite(t).all())
+    assert torch.equal(grads[None][1], grads[0][1]) and torch.equal(grads[None][2], grads[0][2])
+    check("dq (stored dS vs recomputed)", host(grads[None][0]), host(grads[0][0]),
+          BF16_REL_F, BF16_MAX_ABS)
+    wl = dataclasses.replace(CONFIGS["fwdbwd_bf16_L32k"], name="bands", Hq=Hq, Hkv=Hkv, d=d, G=G,
+                             shifted_heads=sh)
+    _group_sums_hold(wl, tdo, grads[0][1], grads[0][2], rope=False)
+    rows = _causal_rows(G)
+    for h in (3, 19, 20, 35, 39):   # units 32..39 form the partial band
+        toks, ro, rl = O.sampled_rows_forward(q, k, v, G, sh, 0, h, 0, rows)
+        tt = torch.from_numpy(toks).cuda()
+        say(f" head {h}: {len(rows)} rows")
+        check("o", host(o[0, tt, h]), ro, BF16_REL_F, BF16_MAX_ABS)
+        check("lse", host(lse[0, h, tt]), rl, BF16_REL_F, BF16_MAX_ABS)
+
+
 # ---------------------------------------------------------------------------
 # Kernel-level invariants.
 # ---------------------------------------------------------------------------
