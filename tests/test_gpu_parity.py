@@ -10,7 +10,7 @@ plus properties that hold at any size over every group.
 Tolerances: bf16 outputs and gradients rel-Frobenius <= 5e-3 and max-abs <=
 2e-2; fp32 path <= 1e-5 for both.  Where a gradient's magnitude puts half a
 bf16 ulp above 2e-2 (dK, dV of the grouped-query workload reach ~10), parity
-is judged on fp32-stored gradients of the same kernels, and the bf16-stored
+is checked on fp32-stored gradients of the same kernels, and the bf16-stored
 result is held to its rounding floor instead.
 """
 
