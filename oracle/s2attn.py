@@ -316,6 +316,64 @@ def sampled_rows_forward(q, k, v, G, shifted_heads, b, h, g, rows_in_group, scal
     return np.array(toks), np.array(os_), np.array(lses)
 
 
+def kv_unit_backward(qs, kg, vg, dos, scale, theta=None):
+    """Gradients of one (b, KV head, group) unit from its gathered rows.
+
+    qs, dos: [r, G, d], the r query heads sharing the KV head, rows in rolled
+    (in-group) order; kg, vg: [G, d] the KV head's rows in the same order;
+    theta: RoPE angles [G, d/2] of those rows at their original positions, or
+    None.  Each query head runs `unit_backward`; dk and dv sum over the r
+    heads.  With RoPE, q and k are rotated first and dq, dk rotated back.
+    Returns dict(dk [G,d], dv [G,d], dq [r,G,d], o [r,G,d], lse [r,G]).
+    """
+
+    def rot(x):
+        return x if theta is None else rope_rotate(x[None, :, None, :], theta)[0, :, 0, :]
+
+    def rot_t(x):
+        return x if theta is None else rope_rotate_transpose(x[None, :, None, :], theta)[0, :, 0, :]
+
+    r, G, d = np.shape(qs)
+    kg = rot(np.asarray(kg, dtype=np.float64))
+    vg = np.asarray(vg, dtype=np.float64)
+    dk = np.zeros((G, d))
+    dv = np.zeros((G, d))
+    dq = np.zeros((r, G, d))
+    o = np.zeros((r, G, d))
+    lse = np.zeros((r, G))
+    for j in range(r):
+        qg = rot(np.asarray(qs[j], dtype=np.float64))
+        dog = np.asarray(dos[j], dtype=np.float64)
+        dqg, dkg, dvg, og, lg = unit_backward(qg, kg, vg, dog, scale)
+        dk += dkg
+        dv += dvg
+        dq[j] = rot_t(dqg)
+        o[j] = og
+        lse[j] = lg
+    return dict(dk=rot_t(dk), dv=dv, dq=dq, o=o, lse=lse)
+
+
+def kv_unit_inputs(q, k, v, do, G, shifted_heads, unit, rope=None):
+    """The gathered rows `kv_unit_backward` takes for unit (b, hk, g).
+
+    Returns (rows, qs, kg, vg, dos, theta): rows are the group's original
+    token indices in rolled order; theta is None without RoPE.  Requires the
+    r query heads of the KV head to share one shift.
+    """
+    b, hk, g = unit
+    B, L, Hq, d = np.shape(q)
+    r = Hq // np.shape(k)[2]
+    heads = list(range(hk * r, (hk + 1) * r))
+    shifts = {head_shift(h, Hq, G, shifted_heads) for h in heads}
+    if len(shifts) != 1:
+        raise ValueError("query heads of one KV head have different shifts")
+    rows = group_members(L, G, shifts.pop(), g)
+    theta = rope_angles(L, d, *rope)[rows] if rope is not None else None
+    qs = np.stack([q[b, rows, h] for h in heads])
+    dos = np.stack([do[b, rows, h] for h in heads])
+    return rows, qs, k[b, rows, hk], v[b, rows, hk], dos, theta
+
+
 def sampled_kv_backward(q, k, v, do, G, shifted_heads, kv_units, scale=None, rope=None):
     """Gradients for selected (b, kv_head, g) units, whose r query heads share a shift.
 
@@ -325,41 +383,18 @@ def sampled_kv_backward(q, k, v, do, G, shifted_heads, kv_units, scale=None, rop
     their groups cover the same rows.
     """
     B, L, Hq, d = q.shape
-    Hkv = k.shape[2]
-    r = Hq // Hkv
+    r = Hq // k.shape[2]
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    theta = rope_angles(L, d, *rope) if rope is not None else None
     res = {}
     for b, hk, g in kv_units:
-        heads = list(range(hk * r, (hk + 1) * r))
-        shifts = {head_shift(h, Hq, G, shifted_heads) for h in heads}
-        if len(shifts) != 1:
-            raise ValueError("query heads of one KV head have different shifts")
-        rows = group_members(L, G, shifts.pop(), g)
-        th = theta[rows] if theta is not None else None
-
-        def rot(x):
-            return x if th is None else rope_rotate(x[None, :, None, :], th)[0, :, 0, :]
-
-        def rot_t(x):
-            return x if th is None else rope_rotate_transpose(x[None, :, None, :], th)[0, :, 0, :]
-
-        kg = rot(np.asarray(k[b, rows, hk], dtype=np.float64))
-        vg = np.asarray(v[b, rows, hk], dtype=np.float64)
-        dk = np.zeros((G, d))
-        dv = np.zeros((G, d))
-        dqs, os_, lses = {}, {}, {}
-        for h in heads:
-            qg = rot(np.asarray(q[b, rows, h], dtype=np.float64))
-            dog = np.asarray(do[b, rows, h], dtype=np.float64)
-            dqg, dkg, dvg, og, lg = unit_backward(qg, kg, vg, dog, scale)
-            dk += dkg
-            dv += dvg
-            dqs[h] = rot_t(dqg)
-            os_[h] = og
-            lses[h] = lg
-        res[(b, hk, g)] = dict(rows=rows, dk=rot_t(dk), dv=dv, dq=dqs, o=os_, lse=lses)
+        rows, qs, kg, vg, dos, theta = kv_unit_inputs(q, k, v, do, G, shifted_heads, (b, hk, g), rope)
+        u = kv_unit_backward(qs, kg, vg, dos, scale, theta)
+        heads = range(hk * r, (hk + 1) * r)
+        res[(b, hk, g)] = dict(rows=rows, dk=u["dk"], dv=u["dv"],
+                               dq={h: u["dq"][j] for j, h in enumerate(heads)},
+                               o={h: u["o"][j] for j, h in enumerate(heads)},
+                               lse={h: u["lse"][j] for j, h in enumerate(heads)})
     return res
 
 

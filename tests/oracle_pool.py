@@ -1,0 +1,96 @@
+"""Run the oracle's per-unit backward over many units in worker processes.
+
+Test infrastructure: the workers call `oracle.s2attn.kv_unit_backward` on the
+rows the parent gathers with `oracle.s2attn.kv_unit_inputs`, one KV unit per
+task, with one BLAS thread each.  The pool is forked once at the start of a
+test session, before any test touches the GPU, so the workers inherit no
+device state; they run numpy only.
+"""
+
+import math
+import multiprocessing as mp
+import os
+
+import numpy as np
+
+from oracle import s2attn as O
+
+_POOL = None
+
+
+def _init_worker():
+    from threadpoolctl import threadpool_limits
+    threadpool_limits(1)
+
+
+def workers():
+    """Worker count: the host cores this process may use, at most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def start():
+    global _POOL
+    if _POOL is None:
+        _POOL = mp.get_context("fork").Pool(workers(), initializer=_init_worker)
+    return _POOL
+
+
+def stop():
+    global _POOL
+    if _POOL is not None:
+        _POOL.close()
+        _POOL.join()
+        _POOL = None
+
+
+def _task(args):
+    key, qs, kg, vg, dos, scale, theta = args
+    return key, O.kv_unit_backward(qs, kg, vg, dos, scale, theta)
+
+
+def kv_units(x, G, shifted_heads, units, rope=None, scale=None):
+    """{(b, hk, g): dict(rows, dk, dv, dq [r,G,d], o [r,G,d], lse [r,G])} for `units`."""
+    q, k, v, do = x["q"], x["k"], x["v"], x["do"]
+    d = q.shape[3]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    rows_of, tasks = {}, []
+    for u in units:
+        rows, qs, kg, vg, dos, theta = O.kv_unit_inputs(q, k, v, do, G, shifted_heads, u, rope)
+        rows_of[u] = rows
+        tasks.append((u, qs, kg, vg, dos, scale, theta))
+    pool = _POOL if _POOL is not None else start()
+    out = {}
+    for key, res in pool.imap_unordered(_task, tasks):
+        res["rows"] = rows_of[key]
+        out[key] = res
+    return out
+
+
+def full_backward(x, G, shifted_heads, rope=None):
+    """Whole reference tensors (o, lse, dq, dk, dv) in float64 from every KV unit."""
+    q, k = x["q"], x["k"]
+    B, L, Hq, d = q.shape
+    Hkv = k.shape[2]
+    r = Hq // Hkv
+    units = [(b, hk, g) for b in range(B) for hk in range(Hkv) for g in range(L // G)]
+    res = kv_units(x, G, shifted_heads, units, rope)
+    o = np.empty((B, L, Hq, d))
+    dq = np.empty((B, L, Hq, d))
+    lse = np.empty((B, Hq, L))
+    dk = np.empty((B, L, Hkv, d))
+    dv = np.empty((B, L, Hkv, d))
+    for (b, hk, g), u in res.items():
+        rows = u["rows"]
+        for j in range(r):
+            h = hk * r + j
+            o[b, rows, h] = u["o"][j]
+            dq[b, rows, h] = u["dq"][j]
+            lse[b, h, rows] = u["lse"][j]
+        dk[b, rows, hk] = u["dk"]
+        dv[b, rows, hk] = u["dv"]
+    return o, lse, dq, dk, dv

@@ -439,3 +439,25 @@ def test_invalid_arguments():
         O.forward(q, k[:, :, :1].repeat(3, 2), v[:, :, :1].repeat(3, 2), 4, 0)  # Hq % Hkv
     with pytest.raises(ValueError):
         O.head_shift(0, 2, 4, 3)
+
+
+def test_pooled_units_equal_the_oracle():
+    """The worker-pool driver the full-size GPU parity tests use returns the
+    oracle's own values: every KV unit through `kv_unit_backward` in worker
+    processes, scattered back, equals `backward` bit for bit (GQA, shifted
+    heads, B = 2, with and without RoPE)."""
+    from tests import oracle_pool
+    rng = np.random.default_rng(12)
+    B, L, Hq, Hkv, d, G, sh = 2, 192, 4, 2, 16, 48, 2
+    x = {n: rng.standard_normal(s) for n, s in (("q", (B, L, Hq, d)), ("k", (B, L, Hkv, d)),
+                                                 ("v", (B, L, Hkv, d)), ("do", (B, L, Hq, d)))}
+    started_here = oracle_pool._POOL is None
+    try:
+        for rope in (None, (100.0, 64)):
+            dq, dk, dv, o, lse = O.backward(x["q"], x["k"], x["v"], x["do"], G, sh, rope=rope)
+            po, plse, pdq, pdk, pdv = oracle_pool.full_backward(x, G, sh, rope)
+            for a, b in ((po, o), (plse, lse), (pdq, dq), (pdk, dk), (pdv, dv)):
+                assert np.array_equal(a, b)
+    finally:
+        if started_here:
+            oracle_pool.stop()
