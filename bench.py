@@ -111,6 +111,9 @@ def parse():
                          "value and ms_per_step then come from the per-step spans, which exclude the flush")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="after timing, run one device copy of this many MiB (counter calibration)")
+    ap.add_argument("--ds-max-mib", type=int, default=96 << 10,
+                    help="bound on the dS tiles the backward keeps in its workspace (MiB; the "
+                         "library default is 16 GiB; 0: dQ recomputes the scores)")
     ap.add_argument("--two-step-sdpa", action="store_true",
                     help="also time the method in its two-step PyTorch form (torch.roll, groups folded "
                          "into the batch, torch SDPA's flash kernel) on the same inputs, as context")
@@ -152,9 +155,11 @@ def main():
     o = torch.empty_like(tq)
     lse = torch.empty((B, Hq, L), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(tq), torch.empty_like(tk), torch.empty_like(tv)
-    opts = s2.make_opts(torch.bfloat16, rope=rope)
+    opts = s2.make_opts(torch.bfloat16, rope=rope, ds_max_mib=args.ds_max_mib)
     fws = s2.s2attn_workspace_size(0, B, L, Hq, Hkv, d, G, opts)
     bws = s2.s2attn_workspace_size(1, B, L, Hq, Hkv, d, G, opts)
+    bws0 = s2.s2attn_workspace_size(1, B, L, Hq, Hkv, d, G,
+                                    s2.make_opts(torch.bfloat16, rope=rope, ds_max_mib=0))
     ws = torch.empty(max(fws, bws, 256), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     sargs = (tq, tk, tv, o, lse, tdo, dq, dk, dv, B, L, Hq, Hkv, d, G, sh, opts, ws, bws, stream)
@@ -246,6 +251,8 @@ def main():
         "config": {"workload": wl.name, "B": B, "L": L, "Hq": Hq, "Hkv": Hkv, "d": d, "G": G,
                    "shifted_heads": sh, "rope": bool(wl.rope), "seed": wl.seed,
                    "parallelism": "single GPU",
+                   "ds_max_mib": args.ds_max_mib,
+                   "dq_from": ("stored dS" if bws > bws0 else "recomputed scores") if wl.backward else None,
                    "caches": f"flushed ({args.flush_mb} MiB written before each step)" if flush is not None else "warm"},
         "pct_of_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "kernels_ms": {k: round(v, 4) for k, v in kms.items()},

@@ -51,12 +51,13 @@ typedef enum {
     S2ATTN_ERR_INVALID_ARG = 1,  /* null pointer, size <= 0, L % G != 0, odd G with shifted
                                     heads, Hq % Hkv != 0, shifted_heads outside [0, Hq],
                                     bad opts (struct_size, dtype, rope fields,
-                                    ds_max_mib < -1) */
+                                    ds_max_mib < -1, residual_split outside [-1, 1]) */
     S2ATTN_ERR_UNSUPPORTED = 2,  /* d not in {64, 128}; backward with shifted_heads % (Hq/Hkv)
                                     != 0 (a KV head shared by shifted and unshifted query
                                     heads); RoPE with float32 inputs; bf16 gradients of
                                     float32 inputs; sizes past the kernels' index ranges:
                                     a (batch, head) plane of L*H*d*2 >= 2^31 bytes,
+                                    a token row of H*d*2 >= 2^24 bytes (H = max(Hq, Hkv)),
                                     L >= 2^24, L*Hq >= 2^31, or a grid of 2^31 or more
                                     workgroups */
     S2ATTN_ERR_WORKSPACE = 3,    /* workspace missing or smaller than s2attn_workspace_size() */
@@ -88,9 +89,19 @@ enum {
  *                Gradients are then w.r.t. the un-rotated q and k.
  *   ds_max_mib   largest region of dS tiles, in MiB, the backward may keep in
  *                its workspace (see s2attn_workspace_size); above it dQ
- *                recomputes the scores instead.  -1 selects the default,
- *                98304 (96 GiB, a third of the MI355X's HBM); 0 never keeps
- *                dS.  Values below -1: S2ATTN_ERR_INVALID_ARG.
+ *                recomputes the scores instead.  Keeping dS trades about
+ *                B*Hq*L*G bytes of workspace for a dQ pass that reads dS back
+ *                instead of recomputing the scores (one product in place of
+ *                three).  -1 selects the default, 16384 (16 GiB); 0 never
+ *                keeps dS.  Values below -1: S2ATTN_ERR_INVALID_ARG.
+ *   residual_split  bf16 backward only.  P and dS enter the dV and dK
+ *                products as bf16 (8 significant bits).  With the split, a
+ *                32 x 32 (query, key) tile whose largest P is at least 1/16
+ *                also adds the products of the residuals x - bf16(x), rounded
+ *                to bf16, so those terms carry about 16 bits; dQ is not
+ *                affected.  1 always, 0 never, -1 (default) when a KV head
+ *                serves several query heads (Hq != Hkv) or G < 4096.  Other
+ *                values: S2ATTN_ERR_INVALID_ARG.
  */
 typedef struct {
     uint32_t struct_size;  /* must equal sizeof(s2attn_opts) */
@@ -101,10 +112,11 @@ typedef struct {
     float rope_base;
     int32_t rope_orig_len;
     int32_t ds_max_mib;
+    int32_t residual_split;
 } s2attn_opts;
 
 /* Defaults: bf16 inputs and gradients, scale 1/sqrt(d), no RoPE, dS kept up
-   to 96 GiB. */
+   to 16 GiB, residual split chosen by shape. */
 void s2attn_opts_init(s2attn_opts* opts);
 
 /*
@@ -118,8 +130,9 @@ int s2attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 /*
  * Backward, bf16 inputs and gradients, scale 1/sqrt(d), no RoPE.
  * Reads q, k, v, o, lse (as written by s2attn_fwd on the same inputs) and
- * dout; writes dq, dk, dv.  delta_ws is caller scratch of 2*B*Hq*L floats
- * (receives -rowsum(dout * o) and lse * log2(e), each [B, Hq, L]).
+ * dout; writes dq, dk, dv.  delta_ws is caller scratch of B*Hq*L floats,
+ * [B, Hq, L]: it receives the row term -rowsum(dout * o) (its contents on
+ * return are that term; nothing else is written to it).
  * Gradient formulas: with P the attention probabilities,
  * dS = P * (dout . v_j - delta), dq = scale dS k, dk = scale dS^T q,
  * dv = P^T dout (summed over query heads per KV head).
@@ -135,13 +148,13 @@ int s2attn_bwd(const void* q, const void* k, const void* v, const void* o,
  * (0 when none).  is_bwd selects the backward.  Returns 0 for invalid
  * arguments as well; the _ex call then reports the error.
  *
- * Backward workspace, each part 256-byte aligned: -delta and lse * log2(e)
- * (2 B Hq L floats); with RoPE the rotated q and k (bf16, the sizes of q and
+ * Backward workspace, each part 256-byte aligned: the row term -delta
+ * (B Hq L floats); with RoPE the rotated q and k (bf16, the sizes of q and
  * k); for bf16 inputs, the dS tiles: per (batch, head, group) the 32 x 32
  * tiles on or below the causal diagonal, padded to whole blocks of 8 query
  * rows: 32 NB (NB + 1) tiles of 2 KB with NB = ceil(ceil(G / 32) / 8), i.e.
  * B Hq (L / G) 32 NB (NB + 1) * 2048 bytes (about B Hq L G bytes), kept only
- * while that is at most opts->ds_max_mib MiB (96 GiB by default).  The dK/dV
+ * while that is at most opts->ds_max_mib MiB (16 GiB by default).  The dK/dV
  * kernel writes dS there and the dQ kernel reads it, so dQ is one product
  * instead of recomputing the scores; above the bound dQ recomputes them.  The
  * plain s2attn_bwd has no workspace and always recomputes.

@@ -44,6 +44,7 @@ class s2attn_opts(ctypes.Structure):
         ("rope_base", ctypes.c_float),
         ("rope_orig_len", ctypes.c_int32),
         ("ds_max_mib", ctypes.c_int32),
+        ("residual_split", ctypes.c_int32),
     ]
 
 

@@ -48,7 +48,36 @@ class Block:
                 "lse": torch.empty(B, Hq, L, dtype=torch.float32, device=device),
                 "u": torch.empty(B * L, 4 * self.r, dtype=bf, device=device)}
 
+    def _check(self, x, params, saved=None, dy=None):
+        """Shapes, dtypes and placement of every tensor, before any library call."""
+        B, L, Hq, Hkv, d = self.shape
+        named = [("x", x)]
+        if tuple(x.shape) != (B, L, Hq * d) or x.dtype != torch.bfloat16:
+            raise ValueError(f"x must be bfloat16 [{B}, {L}, {Hq * d}], got {x.dtype} {tuple(x.shape)}")
+        shapes = param_shapes(Hq, Hkv, d, self.r)
+        for name in PARAM_NAMES:
+            t = params.get(name)
+            if t is None or tuple(t.shape) != shapes[name] or t.dtype != torch.bfloat16:
+                got = None if t is None else (t.dtype, tuple(t.shape))
+                raise ValueError(f"params[{name!r}] must be bfloat16 {shapes[name]}, got {got}")
+            named.append((name, t))
+        if saved is not None:
+            want = {k: (tuple(t.shape), t.dtype) for k, t in self.alloc_saved("meta").items()}
+            for name, (shp, dt) in want.items():
+                t = saved.get(name)
+                if t is None or tuple(t.shape) != shp or t.dtype != dt:
+                    got = None if t is None else (t.dtype, tuple(t.shape))
+                    raise ValueError(f"saved[{name!r}] must be {dt} {shp}, got {got}")
+                named.append(("saved " + name, t))
+        if dy is not None:
+            if dy.shape != x.shape or dy.dtype != x.dtype:
+                raise ValueError("dy must match x in shape and dtype")
+            named.append(("dy", dy))
+        from . import _on_one_gpu
+        _on_one_gpu(named)
+
     def forward(self, x, params, stream=None, ws=None):
+        self._check(x, params)
         saved = self.alloc_saved(x.device)
         y = torch.empty_like(x)
         ws, n = ws if ws is not None else self.workspace(0, x.device)
@@ -56,6 +85,7 @@ class Block:
         return y, saved
 
     def backward(self, x, params, saved, dy, stream=None, ws=None):
+        self._check(x, params, saved, dy)
         B, L, Hq, Hkv, d = self.shape
         grads = {"dx": torch.empty_like(x)}
         for name, shp in param_shapes(Hq, Hkv, d, self.r).items():

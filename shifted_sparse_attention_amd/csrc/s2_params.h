@@ -20,8 +20,7 @@ struct Params {
     void* dq;
     void* dk;
     void* dv;
-    float* delta;   // [B, Hq, L] -rowsum(dout * o), then [B, Hq, L] lse * log2(e)
-    float* lse2;
+    float* delta;   // [B, Hq, L] -rowsum(dout * o)
     // dS tiles of the backward (null: dQ recomputes S and dP).  For unit
     // (b, h, g), tile (q32, k32) with k32 <= q32 < T = ceil(G/32) holds dS of
     // queries 32 q32 .. +31 against keys 32 k32 .. +31, 2 KB.  Query rows go
@@ -83,7 +82,7 @@ __host__ __device__ inline size_t lse_idx(const Params& p, int b, int h, int t) 
 hipError_t launch_fwd_bf16(const Params& p, hipStream_t s);
 hipError_t launch_fwd_f32(const Params& p, hipStream_t s);
 hipError_t launch_bwd_pre(const Params& p, int f32_io, hipStream_t s);
-hipError_t launch_bwd_dkdv_bf16(const Params& p, int grad_f32, hipStream_t s);
+hipError_t launch_bwd_dkdv_bf16(const Params& p, int grad_f32, int split, hipStream_t s);
 hipError_t launch_bwd_dq_bf16(const Params& p, int grad_f32, hipStream_t s);
 hipError_t launch_bwd_dq_ds_bf16(const Params& p, int grad_f32, hipStream_t s);
 hipError_t launch_bwd_dkdv_f32(const Params& p, hipStream_t s);

@@ -20,9 +20,10 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 // The backward keeps dS (bf16, 32 x 32 tiles of each group's causal
 // triangle) for the dQ kernel while the tiles fit the caller's bound; above
-// it, dQ recomputes S and dP instead.  Default bound: 96 GiB, a third of the
-// MI355X's 288 GB of HBM.
-constexpr double kDefaultDsMaxMib = 96.0 * 1024.0;
+// it, dQ recomputes S and dP instead.  Default bound: 16 GiB (about a
+// seventeenth of the MI355X's 288 GB of HBM), enough for 32k tokens of 32
+// heads in groups of 8192 (8.3 GiB); larger regions are the caller's choice.
+constexpr double kDefaultDsMaxMib = 16.0 * 1024.0;
 
 struct Resolved {
     int dtype;       // S2ATTN_BF16 / S2ATTN_F32
@@ -32,7 +33,14 @@ struct Resolved {
     float rope_base;
     int rope_orig_len;
     double ds_max_bytes;  // dS tiles are kept in the workspace up to this size
+    int residual_split;   // -1 auto, 0 off, 1 on (see s2attn_opts)
 };
+
+// The automatic choice of opts.residual_split: on where several query heads
+// share a KV head (dK, dV sum the rounding of r heads' P and dS) or where
+// groups are shorter than 4096 tokens (a larger share of rows sits near the
+// start of a group, where a query sees few keys and P is large).
+bool residual_split_auto(int Hq, int Hkv, int G) { return Hq != Hkv || G < 4096; }
 
 // Sizes shared by forward and backward.
 int check_sizes(int B, int L, int Hq, int Hkv, int d, int G, int shifted_heads) {
@@ -48,9 +56,11 @@ int check_sizes(int B, int L, int Hq, int Hkv, int d, int G, int shifted_heads) 
     const double wgs = (double)B * Hq * (L / G) * ((G + 63) / 64);
     if (wgs > 2147483647.0) return S2ATTN_ERR_UNSUPPORTED;
     if ((double)L * Hq > 2147483647.0) return S2ATTN_ERR_UNSUPPORTED;
-    // Tiles are fetched as a 64-bit (batch, head) base plus 32-bit byte offsets.
+    // Tiles are fetched as a 64-bit (batch, head) base plus 32-bit byte offsets,
+    // a row's offset as a 24-bit by 24-bit product (row index times row bytes).
     const int Hmax = Hq > Hkv ? Hq : Hkv;
     if ((double)L * Hmax * d * 4 > 4294967295.0 || L >= (1 << 24)) return S2ATTN_ERR_UNSUPPORTED;
+    if ((double)Hmax * d * 2 >= (double)(1 << 24)) return S2ATTN_ERR_UNSUPPORTED;
     return S2ATTN_OK;
 }
 
@@ -69,6 +79,7 @@ int resolve_opts(const s2attn_opts* o, int d, Resolved* r) {
     }
     if (o->dtype == S2ATTN_F32 && o->grad_dtype == S2ATTN_BF16) return S2ATTN_ERR_UNSUPPORTED;
     if (o->ds_max_mib < -1) return S2ATTN_ERR_INVALID_ARG;
+    if (o->residual_split < -1 || o->residual_split > 1) return S2ATTN_ERR_INVALID_ARG;
     r->dtype = o->dtype;
     r->grad_dtype = o->grad_dtype;
     r->scale = o->softmax_scale > 0.f ? o->softmax_scale : 1.0f / sqrtf((float)d);
@@ -76,6 +87,7 @@ int resolve_opts(const s2attn_opts* o, int d, Resolved* r) {
     r->rope_base = o->rope_base;
     r->rope_orig_len = o->rope_orig_len;
     r->ds_max_bytes = (o->ds_max_mib < 0 ? kDefaultDsMaxMib : (double)o->ds_max_mib) * 1048576.0;
+    r->residual_split = o->residual_split;
     return S2ATTN_OK;
 }
 
@@ -97,8 +109,8 @@ size_t ds_bytes(int B, int Hq, int L, int G) {
     return (size_t)B * Hq * (L / G) * (32 * NB * (NB + 1)) * 2048;
 }
 
-// Workspace layout: [row terms (bwd): -delta and lse*log2(e) | rotated q | rotated k |
-// dS tiles (bwd, when kept)], each 256-byte aligned.
+// Workspace layout: [row term (bwd): -delta | rotated q | rotated k | dS tiles (bwd,
+// when kept)], each 256-byte aligned.
 struct WsLayout {
     size_t delta_off, delta_bytes;
     size_t rq_off, rq_bytes;
@@ -107,14 +119,14 @@ struct WsLayout {
     size_t total;
 };
 
-// is_bwd: 0 forward, 1 backward with the row terms in the workspace, 2 backward
-// with the row terms supplied separately (the plain entry point: no dS tiles).
+// is_bwd: 0 forward, 1 backward with the row term in the workspace, 2 backward
+// with the row term supplied separately (the plain entry point: no dS tiles).
 WsLayout ws_layout(int is_bwd, int B, int L, int Hq, int Hkv, int d, int G, const Resolved& r) {
     WsLayout w{};
     size_t off = 0;
     if (is_bwd == 1) {
         w.delta_off = off;
-        w.delta_bytes = 2 * (size_t)B * Hq * L * sizeof(float);
+        w.delta_bytes = (size_t)B * Hq * L * sizeof(float);
         off += align_up(w.delta_bytes);
     }
     if (r.rope) {
@@ -237,7 +249,6 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const f
     p.dk = dk;
     p.dv = dv;
     p.delta = delta;
-    p.lse2 = delta + (size_t)B * Hq * L;
     p.ds = wl.ds_bytes ? base + wl.ds_off : nullptr;
 
     char* rq = base + wl.rq_off;
@@ -254,8 +265,9 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const f
     }
     const int gf = r.grad_dtype == S2ATTN_F32;
     if (stages & kStageDkdv) {
+        const int split = r.residual_split >= 0 ? r.residual_split : residual_split_auto(Hq, Hkv, G);
         hipError_t e = r.dtype == S2ATTN_F32 ? s2::launch_bwd_dkdv_f32(p, stream)
-                                              : s2::launch_bwd_dkdv_bf16(p, gf, stream);
+                                              : s2::launch_bwd_dkdv_bf16(p, gf, split, stream);
         if (e != hipSuccess) return S2ATTN_ERR_HIP;
     }
     if (stages & kStageDq) {
@@ -297,6 +309,7 @@ void s2attn_opts_init(s2attn_opts* opts) {
     opts->rope_base = 10000.f;
     opts->rope_orig_len = 4096;
     opts->ds_max_mib = -1;
+    opts->residual_split = -1;
 }
 
 int s2attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int L,

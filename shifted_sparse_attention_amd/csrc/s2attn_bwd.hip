@@ -9,6 +9,8 @@
 // (dK, dV), another owns a query tile and loops over the keys before it (dQ).
 #include <math.h>
 
+#include <type_traits>
+
 #include "s2_device.h"
 
 namespace s2 {
@@ -27,8 +29,7 @@ __device__ __forceinline__ size_t ds_tile(int q32, int k32) {
 // ---------------------------------------------------------------------------
 // The row term, stored negated: p.delta[b, h, t] = -sum_c dO[b, t, h, c] *
 // O[b, t, h, c] (fp32; the dK/dV kernel starts its dP accumulation from it,
-// so the MFMA yields dP - delta directly), and the LSE in base 2,
-// lse2[b, h, t] = lse[b, h, t] * log2(e), for exp2 in the loops.
+// so the MFMA yields dP - delta directly).
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(Params p, long n_rows) {
@@ -51,9 +52,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(Params p, long n_rows) {
         const long bt = row / p.Hq;
         const int t = (int)(bt % p.L);
         const int b = (int)(bt / p.L);
-        const size_t li = lse_idx(p, b, h, t);
-        p.delta[li] = -acc;
-        p.lse2[li] = p.lse[li] * kLog2e;
+        p.delta[lse_idx(p, b, h, t)] = -acc;
     }
 }
 
@@ -247,8 +246,17 @@ __device__ __forceinline__ void reduce_store(const Params& p, f32x16 (&acc)[D / 
 constexpr int DKV_WAVES = 8;
 constexpr int DKV_BK = 128;
 constexpr int DKV_BQ = 64;
+// P and dS enter the dV and dK products as bf16, each rounded by up to 2^-9
+// of itself.  The terms of a query row with the largest P dominate those
+// sums (the first rows of a group, where a query sees few keys, or rows with
+// concentrated attention), so a 32 x 32 tile whose largest P reaches 1/16
+// adds the products of the residuals x - bf16(x), rounded to bf16 in turn:
+// about 16 bits of P and dS there.  Tiles below it hold terms at least 16
+// times smaller than the largest of their row.  With standard-normal inputs
+// at the 32k-token shapes (groups of 8192) about 0.13% of tiles qualify.
+constexpr float kSplitP = 0.0625f;
 
-template <int D, bool GRAD_F32>
+template <int D, bool GRAD_F32, bool SPLIT>
 __global__ __launch_bounds__(64 * DKV_WAVES) void bwd_dkdv_bf16_kernel(Params p, int n_kt) {
     constexpr int KS = D / 16;
     constexpr int CB = D / 32;
@@ -256,10 +264,18 @@ __global__ __launch_bounds__(64 * DKV_WAVES) void bwd_dkdv_bf16_kernel(Params p,
     constexpr int KTILE = DKV_BK * D * 2;            // the workgroup's K (or V) rows
     constexpr int NCH = TILE / 1024;
     constexpr int KNCH = KTILE / 1024;
-    constexpr int BUF = 2 * TILE + 2 * DKV_BQ * 4;   // Q, dO, lse2, delta
+    constexpr int BUF = 2 * TILE + 2 * DKV_BQ * 4;   // Q, dO, lse, delta
     constexpr int RED = CB * 4 * 64 * 16;            // one wave's fp32 partial (dK or dV)
     static_assert(4 * RED <= 2 * BUF + 2 * KTILE, "reduction area");
-    __shared__ __attribute__((aligned(1024))) char smem[2 * KTILE + 2 * BUF];
+    // With SPLIT, the residual stash of split steps (kSplitP): per wave 4 KB,
+    // the P and dS residuals of its 32 x 32 tile.  Where that does not fit
+    // beside the buffers (D = 128), the first 1 KB of the dS residual goes to
+    // the K rows' channels held in registers (kreg), whose LDS copy is not
+    // read.
+    constexpr int NOSTASH = 2 * KTILE + 2 * BUF;
+    constexpr bool DS0_IN_K = SPLIT && NOSTASH + DKV_WAVES * 4096 > 160 * 1024;
+    constexpr int STASH_W = !SPLIT ? 0 : DS0_IN_K ? 3072 : 4096;   // per wave, beside the buffers
+    __shared__ __attribute__((aligned(1024))) char smem[NOSTASH + DKV_WAVES * STASH_W];
     char* sKt = smem;
     char* sVt = smem + KTILE;
     char* bufs = smem + 2 * KTILE;
@@ -299,7 +315,7 @@ __global__ __launch_bounds__(64 * DKV_WAVES) void bwd_dkdv_bf16_kernel(Params p,
             dma16((isv ? v : k) + plane, off, (isv ? sVt : sKt) + cc * 1024);
         }
     }
-    // Q, dO, lse2, delta of a step: query head h, tile qt_first + t.  Steps
+    // Q, dO, lse, delta of a step: query head h, tile qt_first + t.  Steps
     // walk t = 0 .. nq - 1 for each query head of the KV head in turn.  Rows
     // past the group are clamped to its last row and masked in the loop.
     constexpr int NSLOT = 2 * NCH / DKV_WAVES;  // 1 KB chunks per wave per tile; Q first, then dO
@@ -316,8 +332,8 @@ __global__ __launch_bounds__(64 * DKV_WAVES) void bwd_dkdv_bf16_kernel(Params p,
             const uint32_t off = row_off(w.g, p.G, q0 + sl.row, s, p.L, qrowb) + sl.colb;
             dma16((isg ? dout : q) + plane, off, base + (isg ? TILE : 0) + cc * 1024);
         }
-        if (wave < 2) {  // LSE (base 2) and delta of the tile's 64 queries
-            const float* rb = (wave == 0 ? p.lse2 : p.delta) + ((size_t)w.b * p.Hq + h) * p.L;
+        if (wave < 2) {  // LSE and delta of the tile's 64 queries
+            const float* rb = (wave == 0 ? p.lse : p.delta) + ((size_t)w.b * p.Hq + h) * p.L;
             const uint32_t off = 4u * (uint32_t)orig_row(w.g, p.G, min(q0 + lane, p.G - 1), s, p.L);
             dma4(rb, off, base + 2 * TILE + wave * DKV_BQ * 4);
         }
@@ -327,7 +343,9 @@ __global__ __launch_bounds__(64 * DKV_WAVES) void bwd_dkdv_bf16_kernel(Params p,
     // The first KREG channel blocks of this wave's K rows stay in registers
     // (the B operands of S for k-steps ks < KREG): fewer LDS reads per step,
     // within the register budget of two waves per SIMD.
-    constexpr int KREG = KS / 2;
+    // (Two 16-channel blocks: with four the register budget spills.)
+    constexpr int KREG = 2;
+    static_assert(!DS0_IN_K || (D == 128 && KREG == 2), "the K rows' unread block is 64 bytes of a row");
     bf16x8 kreg[KREG];
     wait_vmem();
     __syncthreads();
@@ -350,6 +368,25 @@ __global__ __launch_bounds__(64 * DKV_WAVES) void bwd_dkdv_bf16_kernel(Params p,
                                : static_cast<char*>(p.ds) +
                                      (((size_t)w.b * p.Hq + h) * p.n_g + w.g) * TT * 2048;
     };
+    // This lane's 16-byte slot for part kk (0, 1) of the P (which = 0) or dS
+    // (which = 1) residual: chunk 64 kk + lane of that tile.  At D = 128 the
+    // dS residual's part 0 sits in K row r = 16 wave + lane / 4, in the 64
+    // bytes holding channels 0..31 (logical slots 0..3, physically slots
+    // 4 (r & 3) .. + 3 under the row's XOR swizzle).  Formed where it is used
+    // (the empty asm keeps the addresses out of the loop's live set).
+    auto res_slot = [&](int which, int kk) -> char* {
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        char* free_w = smem + NOSTASH + wave * STASH_W;
+        if constexpr (DS0_IN_K) {
+            if (which == 0) return free_w + 1024 * kk + 16 * ln;
+            if (kk == 1) return free_w + 2048 + 16 * ln;
+            const int r = 16 * wave + ln / 4;
+            return sKt + r * (D * 2) + 64 * (r & 3) + 16 * (ln % 4);
+        } else {
+            return free_w + 2048 * which + 1024 * kk + 16 * ln;
+        }
+    };
     int h = hk * p.r, t = 0;   // current step
     char* ds_base = ds_head(h);
     // dS stores of the previous step still in flight (0 or 2; wave-uniform):
@@ -361,6 +398,12 @@ __global__ __launch_bounds__(64 * DKV_WAVES) void bwd_dkdv_bf16_kernel(Params p,
             wait_vmem_n<2>();
         else
             wait_vmem();
+        // Wave 0 loaded this step's LSE (natural log) into LDS: turn it into
+        // base 2 in place before the barrier publishes the buffer.
+        if (wave == 0) {
+            float* l = reinterpret_cast<float*>(bufs + (it & 1) * BUF + 2 * TILE) + lane;
+            *l *= kLog2e;
+        }
         __syncthreads();
         if (it + 1 < n_it) {
             if (t + 1 < nq)
@@ -380,8 +423,8 @@ __global__ __launch_bounds__(64 * DKV_WAVES) void bwd_dkdv_bf16_kernel(Params p,
         const bool masked = (qb < kw + 31) || (qb + 32 > p.G);
         const char* sQ = bufs + (it & 1) * BUF + 32 * qh * D * 2;
         const char* sO = sQ + TILE;
-        const float* s_l2 = reinterpret_cast<const float*>(bufs + (it & 1) * BUF + 2 * TILE) + 32 * qh;
-        const float* s_dl = s_l2 + DKV_BQ;
+        const float* s_lse = reinterpret_cast<const float*>(bufs + (it & 1) * BUF + 2 * TILE) + 32 * qh;  // base 2
+        const float* s_dl = s_lse + DKV_BQ;
 
         // dP accumulates onto -delta of its query row (element i is row
         // 8(i/4) + 4hh + i%4), so pacc ends as dP - delta.
@@ -418,7 +461,7 @@ __global__ __launch_bounds__(64 * DKV_WAVES) void bwd_dkdv_bf16_kernel(Params p,
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int r0 = 8 * j + 4 * hh;
-                const f32x4 l4 = *reinterpret_cast<const f32x4*>(&s_l2[r0]);
+                const f32x4 l4 = *reinterpret_cast<const f32x4*>(&s_lse[r0]);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int i = 4 * j + e;
@@ -448,6 +491,14 @@ __global__ __launch_bounds__(64 * DKV_WAVES) void bwd_dkdv_bf16_kernel(Params p,
             pb[kk] = to_bf16x8(t1);
             db[kk] = to_bf16x8(t2);
         }
+        // A tile holding a probability of at least 1/16 also feeds the
+        // rounding residuals of P and dS (their next 8 bits, bf16(x -
+        // bf16(x))) to dV and dK; see kSplitP.
+        // (P >= 0, so the largest P has the largest bit pattern.)
+        uint32_t pmax = __float_as_uint(sacc[0]);
+#pragma unroll
+        for (int i = 1; i < 16; ++i) pmax = max(pmax, __float_as_uint(sacc[i]));
+        const bool split = SPLIT && __builtin_amdgcn_ballot_w64(pmax >= __float_as_uint(kSplitP)) != 0;
         if (it_ds != nullptr && qb < p.G) {
             // dS tile out for the dQ kernel, in register order: db[kk] of
             // every lane at byte 1024 kk + 16 lane, so each store writes 1 KB
@@ -457,22 +508,50 @@ __global__ __launch_bounds__(64 * DKV_WAVES) void bwd_dkdv_bf16_kernel(Params p,
             __builtin_nontemporal_store(__builtin_bit_cast(u32x4, db[1]), out + 64);
             ds_inflight = 2;
         }
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-            const int col = 32 * cb + 16 * (g16 & 1) + 4 * (jj & 3);
+        // The residual tiles of a split step wait in LDS (see res_slot), so
+        // that no register stays live across the main products for them.
+        if (split) {
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                const int row = 16 * kk + 4 * hh + (jj >> 2);
-                const bf16x8 go = cat(ld_lds_tr(sO, tile_off<D>(row, col)),
-                                      ld_lds_tr(sO, tile_off<D>(row + 8, col)));
-                dv[cb] = mfma32(go, pb[kk], dv[cb]);
-                const bf16x8 qq = cat(ld_lds_tr(sQ, tile_off<D>(row, col)),
-                                      ld_lds_tr(sQ, tile_off<D>(row + 8, col)));
-                dk[cb] = mfma32(qq, db[kk], dk[cb]);
+                float t1[8], t2[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    t1[i] = sacc[8 * kk + i] - (float)pb[kk][i];
+                    t2[i] = pacc[8 * kk + i] - (float)db[kk][i];
+                }
+                *reinterpret_cast<bf16x8*>(res_slot(0, kk)) = to_bf16x8(t1);
+                *reinterpret_cast<bf16x8*>(res_slot(1, kk)) = to_bf16x8(t2);
             }
         }
-        // Transposed reads 12 ahead, then two per MFMA.
-        {
+        // dV^T += dO^T P and dK^T += Q^T dS (bf16 P and dS as B operands;
+        // with `lo`, their residuals from the stash).
+        auto grad_products = [&](bool lo) {
+            bf16x8 bp[2], bd[2];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                if (lo) {
+                    bp[kk] = *reinterpret_cast<const bf16x8*>(res_slot(0, kk));
+                    bd[kk] = *reinterpret_cast<const bf16x8*>(res_slot(1, kk));
+                } else {
+                    bp[kk] = pb[kk];
+                    bd[kk] = db[kk];
+                }
+            }
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) {
+                const int col = 32 * cb + 16 * (g16 & 1) + 4 * (jj & 3);
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    const int row = 16 * kk + 4 * hh + (jj >> 2);
+                    const bf16x8 go = cat(ld_lds_tr(sO, tile_off<D>(row, col)),
+                                          ld_lds_tr(sO, tile_off<D>(row + 8, col)));
+                    dv[cb] = mfma32(go, bp[kk], dv[cb]);
+                    const bf16x8 qq = cat(ld_lds_tr(sQ, tile_off<D>(row, col)),
+                                          ld_lds_tr(sQ, tile_off<D>(row + 8, col)));
+                    dk[cb] = mfma32(qq, bd[kk], dk[cb]);
+                }
+            }
+            // Transposed reads 12 ahead, then two per MFMA.
             constexpr int NR = 8 * CB, NM = 4 * CB, AHEAD = 12, PAIRS = (NR - AHEAD) / 2;
             __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
 #pragma unroll
@@ -481,7 +560,9 @@ __global__ __launch_bounds__(64 * DKV_WAVES) void bwd_dkdv_bf16_kernel(Params p,
                 __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             }
             __builtin_amdgcn_sched_group_barrier(0x008, NM - PAIRS, 0);
-        }
+        };
+        grad_products(false);
+        if (split) grad_products(true);
     }
 
     // Sum the two query halves (waves 4..7 hand their partials to waves 0..3),
@@ -576,10 +657,10 @@ __global__ __launch_bounds__(64 * DQ_WAVES) void bwd_dq_bf16_kernel(Params p, in
             gf[ks] = __builtin_bit_cast(bf16x8, b);
         }
     }
-    float lse2 = 0.f, dl = 0.f;
+    float lse2 = 0.f, dl = 0.f;  // LSE in base 2, -delta
     if (q_valid) {
         const size_t li = lse_idx(p, w.b, w.h, q_t);
-        lse2 = p.lse2[li];
+        lse2 = p.lse[li] * kLog2e;
         dl = p.delta[li];
     }
     f32x16 dq[CB];
@@ -1007,14 +1088,19 @@ hipError_t launch_rope_prepass(const Params& p, void* q_out, void* k_out, hipStr
     return hipGetLastError();
 }
 
-template <int D, bool GF>
+template <int D, bool GF, bool SPLIT>
 static void launch_dkdv_t(const Params& p0, hipStream_t st) {
     const int n_kt = (p0.G + DKV_BK - 1) / DKV_BK;
     const long blocks = (long)p0.B * p0.Hkv * p0.n_g * n_kt;
     Params p = p0;  // band: Q and dO of the r query heads of the unit
     p.band = dispatch_band(p.B * p.Hkv * p.n_g, (size_t)p.r * p.G * p.d * 4);
-    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, GF>), dim3(blocks), dim3(64 * DKV_WAVES), 0, st, p,
-                       n_kt);
+    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, GF, SPLIT>), dim3(blocks), dim3(64 * DKV_WAVES), 0,
+                       st, p, n_kt);
+}
+
+template <int D, bool GF>
+static void launch_dkdv_split(const Params& p, bool split, hipStream_t st) {
+    split ? launch_dkdv_t<D, GF, true>(p, st) : launch_dkdv_t<D, GF, false>(p, st);
 }
 
 template <int D, bool GF>
@@ -1027,11 +1113,11 @@ static void launch_dq_t(const Params& p0, hipStream_t st) {
                        n_qt);
 }
 
-hipError_t launch_bwd_dkdv_bf16(const Params& p, int grad_f32, hipStream_t st) {
+hipError_t launch_bwd_dkdv_bf16(const Params& p, int grad_f32, int split, hipStream_t st) {
     if (p.d == 128)
-        grad_f32 ? launch_dkdv_t<128, true>(p, st) : launch_dkdv_t<128, false>(p, st);
+        grad_f32 ? launch_dkdv_split<128, true>(p, split, st) : launch_dkdv_split<128, false>(p, split, st);
     else
-        grad_f32 ? launch_dkdv_t<64, true>(p, st) : launch_dkdv_t<64, false>(p, st);
+        grad_f32 ? launch_dkdv_split<64, true>(p, split, st) : launch_dkdv_split<64, false>(p, split, st);
     return hipGetLastError();
 }
 

@@ -10,6 +10,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import shifted_sparse_attention_amd as s2
 from shifted_sparse_attention_amd import _lib as L
@@ -63,6 +64,7 @@ def test_opts_defaults():
     assert o.dtype == L.S2ATTN_BF16 and o.grad_dtype == L.S2ATTN_BF16
     assert o.softmax_scale == 0.0 and o.rope == 0
     assert o.rope_base == 10000.0 and o.rope_orig_len == 4096
+    assert o.ds_max_mib == -1 and o.residual_split == -1
 
 
 GOOD = dict(B=1, L=256, Hq=4, Hkv=4, d=64, G=64, sh=2)
@@ -105,6 +107,8 @@ INV, UNS, WS = L.S2ATTN_ERR_INVALID_ARG, L.S2ATTN_ERR_UNSUPPORTED, L.S2ATTN_ERR_
     (dict(L=255, G=51, sh=1), INV),                        # odd G with shifted heads
     (dict(d=96), UNS), (dict(d=32), UNS),
     (dict(L=1 << 22, G=1 << 22, sh=0), UNS),   # one (batch, head) plane past 32-bit offsets
+    # a token row of H*d*2 = 2^24 bytes: past the 24-bit row-offset product
+    (dict(L=64, G=64, Hq=65536, Hkv=65536, d=128, sh=0), UNS),
 ])
 def test_fwd_argument_checks(kw, want):
     assert fwd(**kw) == want
@@ -147,12 +151,23 @@ def test_opts_checks():
     assert bwd_ex(o) == UNS
 
 
+def test_residual_split_option_checks():
+    for val, want in ((-2, INV), (2, INV)):
+        o = s2.s2attn_opts_init()
+        o.residual_split = val
+        assert bwd_ex(o, FAKE, 1 << 20, Hkv=2) == want
+        assert fwd_ex(o) == want
+    assert s2.make_opts(torch.bfloat16, residual_split=True).residual_split == 1
+    assert s2.make_opts(torch.bfloat16, residual_split=False).residual_split == 0
+    assert s2.make_opts(torch.bfloat16).residual_split == -1
+
+
 def test_workspace_sizes_and_checks():
     o = s2.s2attn_opts_init()
     B, Ln, Hq, Hkv, d, G = 1, 256, 4, 2, 64, 64
     assert s2.s2attn_workspace_size(0, B, Ln, Hq, Hkv, d, G, o) == 0
     r256 = lambda x: (x + 255) // 256 * 256
-    delta = 2 * B * Hq * Ln * 4     # delta and lse * log2(e)
+    delta = B * Hq * Ln * 4         # the row term -delta, [B, Hq, L] fp32
     # dS tiles: per (batch, head, group) the 32 x 32 bf16 tiles of the causal
     # triangle, padded to whole blocks of 8 query rows (NB blocks)
     def ds_bytes(B, Hq, L, G):
@@ -166,7 +181,7 @@ def test_workspace_sizes_and_checks():
     Gr = 80                          # ragged last tile row (T = 3, one block of 8 rows)
     dsr = ds_bytes(B, Hq, 240, Gr)
     assert dsr == B * Hq * 3 * 64 * 2048
-    assert s2.s2attn_workspace_size(1, B, 240, Hq, Hkv, d, Gr, o) == r256(2 * B * Hq * 240 * 4) + r256(dsr)
+    assert s2.s2attn_workspace_size(1, B, 240, Hq, Hkv, d, Gr, o) == r256(B * Hq * 240 * 4) + r256(dsr)
     o.rope = 1
     rq, rk = B * Ln * Hq * d * 2, B * Ln * Hkv * d * 2
     assert s2.s2attn_workspace_size(0, B, Ln, Hq, Hkv, d, G, o) == r256(rq) + r256(rk)
@@ -183,7 +198,7 @@ def test_workspace_sizes_and_checks():
 
 
 def test_ds_tiles_bound():
-    """dS tiles are kept while they fit opts.ds_max_mib (default 96 GiB)."""
+    """dS tiles are kept while they fit opts.ds_max_mib (default 16 GiB)."""
     r256 = lambda x: (x + 255) // 256 * 256
     def ds_bytes(B, Hq, L, G):
         NB = ((G + 31) // 32 + 7) // 8
@@ -197,21 +212,29 @@ def test_ds_tiles_bound():
         return s2.s2attn_workspace_size(1, B, Ln, H, H, 128, G, o)
     assert s2.s2attn_opts_init().ds_max_mib == -1
     # L = 32768, G = 8192, 32 heads: 8448 MiB of tiles
-    rows = r256(2 * 32 * 32768 * 4)
+    rows = r256(32 * 32768 * 4)
     ds32 = ds_bytes(1, 32, 32768, 8192)
     assert ds32 == 8448 << 20
     assert ws(1, 32768, 32, 8192) == rows + ds32
     assert ws(1, 32768, 32, 8192, mib=8448) == rows + ds32     # exactly at the bound
     assert ws(1, 32768, 32, 8192, mib=8447) == rows            # one MiB short: recompute
     assert ws(1, 32768, 32, 8192, mib=0) == rows
-    # L = 102400, G = 25600 with RoPE: 78.9 GiB of tiles, under the 96 GiB default
+    # L = 102400, G = 25600 with RoPE: 78.9 GiB of tiles, over the 16 GiB
+    # default (recompute) unless the caller raises the bound
     rot = r256(102400 * 32 * 128 * 2)
     ds100 = ds_bytes(1, 32, 102400, 25600)
     assert 64 << 30 < ds100 < 96 << 30
-    assert ws(1, 102400, 32, 25600, rope=True) == r256(2 * 32 * 102400 * 4) + 2 * rot + ds100
-    assert ws(1, 102400, 32, 25600, mib=32 << 10, rope=True) == r256(2 * 32 * 102400 * 4) + 2 * rot
-    # four times that (B = 4) exceeds the default: recompute
-    assert ws(4, 102400, 32, 25600) == r256(2 * 4 * 32 * 102400 * 4)
+    rows100 = r256(32 * 102400 * 4)
+    assert ws(1, 102400, 32, 25600, rope=True) == rows100 + 2 * rot
+    assert ws(1, 102400, 32, 25600, mib=96 << 10, rope=True) == rows100 + 2 * rot + ds100
+    assert ws(1, 102400, 32, 25600, mib=32 << 10, rope=True) == rows100 + 2 * rot
+    # the grouped-query 32k shape (64 query heads): 16.5 GiB of tiles, just over the default
+    ds_gqa = ds_bytes(1, 64, 32768, 8192)
+    assert 16 << 30 < ds_gqa
+    o = s2.s2attn_opts_init()
+    assert s2.s2attn_workspace_size(1, 1, 32768, 64, 8, 128, 8192, o) == r256(64 * 32768 * 4)
+    o.ds_max_mib = 17 << 10
+    assert s2.s2attn_workspace_size(1, 1, 32768, 64, 8, 128, 8192, o) == r256(64 * 32768 * 4) + ds_gqa
     # below -1 is an argument error (workspace size 0, the call reports it)
     o = s2.s2attn_opts_init()
     o.ds_max_mib = -2
@@ -306,3 +329,55 @@ def test_block_pointer_and_workspace_checks():
     assert _block_fwd(cfg, ws_bytes=s2.s2block_workspace_size(0, cfg) - 1) == WS
     assert _block_bwd(cfg, grads=dict(BLOCK_GRADS, dbq=None)) == INV
     assert _block_bwd(cfg, ws_bytes=1024) == WS
+
+
+# ---------------------------------------------------------------------------
+# The Python binding checks every tensor before any library call.
+# ---------------------------------------------------------------------------
+
+def _bf(*shape):
+    return torch.zeros(shape, dtype=torch.bfloat16)
+
+
+def test_binding_rejects_host_tensors():
+    q, k = _bf(1, 64, 4, 64), _bf(1, 64, 2, 64)
+    with pytest.raises(ValueError, match="CUDA tensor"):
+        s2.forward(q, k, k.clone(), 16, 2)
+
+
+def test_binding_rejects_mixed_dtypes_and_layouts():
+    q, k, v = _bf(1, 64, 4, 64), _bf(1, 64, 2, 64), _bf(1, 64, 2, 64)
+    with pytest.raises(ValueError, match="dtype"):
+        s2.forward(q, k.float(), v, 16, 2)
+    with pytest.raises(ValueError, match="contiguous"):
+        s2.forward(q.transpose(1, 2).contiguous().transpose(1, 2), k, v, 16, 2)
+    o, lse = _bf(1, 64, 4, 64), torch.zeros(1, 4, 64)
+    dout = _bf(1, 64, 4, 64)
+    with pytest.raises(ValueError, match="lse"):
+        s2.backward(q, k, v, o, lse.bfloat16(), dout, 16, 2)
+    with pytest.raises(ValueError, match="dout"):
+        s2.backward(q, k, v, o, lse, dout.float(), 16, 2)
+    with pytest.raises(ValueError, match="o must"):
+        s2.backward(q, k, v, o.float(), lse, dout, 16, 2)
+    # the gradient of a sum: a stride-0 expanded dout
+    expanded = torch.ones((), dtype=torch.bfloat16).expand(1, 64, 4, 64)
+    with pytest.raises(ValueError, match="dout must be contiguous"):
+        s2.backward(q, k, v, o, lse, expanded, 16, 2)
+
+
+def test_block_binding_checks_shapes():
+    from shifted_sparse_attention_amd.block import Block, param_shapes
+    blk = Block(1, 64, 4, 2, 16, 16, 2, lora_rank=8)
+    params = {n: torch.zeros(s, dtype=torch.bfloat16) for n, s in param_shapes(4, 2, 16, 8).items()}
+    with pytest.raises(ValueError, match="x must be"):
+        blk.forward(_bf(1, 64, 32), params)
+    bad = dict(params, bo=torch.zeros(64, 4, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="bo"):
+        blk.forward(_bf(1, 64, 64), bad)
+    with pytest.raises(ValueError, match="CUDA tensor"):
+        blk.forward(_bf(1, 64, 64), params)
+    saved = blk.alloc_saved("cpu")
+    with pytest.raises(ValueError, match="dy must"):
+        blk.backward(_bf(1, 64, 64), params, saved, _bf(1, 64, 32))
+    with pytest.raises(ValueError, match="lse"):
+        blk.backward(_bf(1, 64, 64), params, dict(saved, lse=saved["lse"].bfloat16()), _bf(1, 64, 64))
