@@ -143,6 +143,30 @@ int s2attn_bwd(const void* q, const void* k, const void* v, const void* o,
                int B, int L, int Hq, int Hkv, int d, int G, int shifted_heads,
                hipStream_t stream);
 
+/* Row-term floats (B * Hq * L) s2attn_bwd_noalloc's device array holds. */
+#define S2ATTN_NOALLOC_MAX_ROWS (1u << 23)
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the plain
+ * backward (bf16, scale 1/sqrt(d), no RoPE, the same kernels and results as
+ * s2attn_bwd) without delta_ws.  The row term lives in a device array inside
+ * the library, S2ATTN_NOALLOC_MAX_ROWS floats (32 MiB) on each GPU it runs on,
+ * held until the process ends; the call itself allocates nothing.
+ * B * Hq * L above S2ATTN_NOALLOC_MAX_ROWS: S2ATTN_ERR_WORKSPACE (after the
+ * argument checks of s2attn_bwd, which come first and run on the host).
+ * Every call on one GPU uses that GPU's one array: calls whose execution
+ * overlaps on one GPU (other streams, other threads) race and must be
+ * serialised by the caller.  Nothing needs clearing between calls: each
+ * call's row-term kernel writes every element its gradient kernels read.
+ * The array's address is looked up once per device, on the first call with
+ * that device current (a HIP runtime query; not inside the stream's work).
+ */
+int s2attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                       const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                       int B, int L, int Hq, int Hkv, int d, int G, int shifted_heads,
+                       hipStream_t stream);
+
 /*
  * Bytes of workspace the _ex entry points need for these sizes and options
  * (0 when none).  is_bwd selects the backward.  Returns 0 for invalid

@@ -83,6 +83,7 @@ _SIGS = {
     "s2attn_opts_init": (None, [ctypes.POINTER(s2attn_opts)]),
     "s2attn_fwd": (_ci, [_vp, _vp, _vp, _vp, _vp] + [_ci] * 7 + [_vp]),
     "s2attn_bwd": (_ci, [_vp] * 10 + [_ci] * 7 + [_vp]),
+    "s2attn_bwd_noalloc": (_ci, [_vp] * 9 + [_ci] * 7 + [_vp]),
     "s2attn_workspace_size": (_sz, [_ci] * 7 + [ctypes.POINTER(s2attn_opts)]),
     "s2attn_fwd_ex": (_ci, [_vp] * 5 + [_ci] * 7 + [ctypes.POINTER(s2attn_opts), _vp, _sz, _vp]),
     "s2attn_bwd_ex": (_ci, [_vp] * 9 + [_ci] * 7 + [ctypes.POINTER(s2attn_opts), _vp, _sz, _vp]),
@@ -177,6 +178,16 @@ def s2attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta_ws, B, L, Hq, Hkv, d, G,
     _check(lib().s2attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
                             _ptr(dq), _ptr(dk), _ptr(dv), _ptr(delta_ws),
                             B, L, Hq, Hkv, d, G, shifted_heads, _stream(stream)), "s2attn_bwd")
+
+
+S2ATTN_NOALLOC_MAX_ROWS = 1 << 23
+
+
+def s2attn_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, B, L, Hq, Hkv, d, G, shifted_heads,
+                       stream=None):
+    _check(lib().s2attn_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
+                                    _ptr(dq), _ptr(dk), _ptr(dv), B, L, Hq, Hkv, d, G,
+                                    shifted_heads, _stream(stream)), "s2attn_bwd_noalloc")
 
 
 def s2attn_workspace_size(is_bwd, B, L, Hq, Hkv, d, G, opts=None):

@@ -89,6 +89,12 @@ hipError_t launch_bwd_dkdv_f32(const Params& p, hipStream_t s);
 hipError_t launch_bwd_dq_f32(const Params& p, hipStream_t s);
 hipError_t launch_rope_prepass(const Params& p, void* q_out, void* k_out, hipStream_t s);
 
+// The plain backward (s2attn_bwd) with the row term in `delta`; with launch = 0
+// only its host checks run (delta may then be null) and nothing is enqueued.
+int bwd_plain(const void* q, const void* k, const void* v, const void* o, const float* lse,
+              const void* dout, void* dq, void* dk, void* dv, float* delta, int B, int L, int Hq,
+              int Hkv, int d, int G, int shifted_heads, hipStream_t stream, int launch);
+
 // The checks s2attn_fwd_ex (is_bwd = 0) or s2attn_bwd_ex (is_bwd = 1) run on
 // their sizes and options, without pointers: for callers that must validate
 // a whole sequence of work before enqueueing any of it.

@@ -283,6 +283,17 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const f
 
 namespace s2 {
 
+int bwd_plain(const void* q, const void* k, const void* v, const void* o, const float* lse,
+              const void* dout, void* dq, void* dk, void* dv, float* delta, int B, int L, int Hq,
+              int Hkv, int d, int G, int shifted_heads, hipStream_t stream, int launch) {
+    // Without a launch only the host checks run; any aligned non-null address
+    // stands in for the row term's buffer then.
+    float* dl = launch ? delta : reinterpret_cast<float*>(kAlign);
+    if (!dl) return S2ATTN_ERR_INVALID_ARG;
+    return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, dl, B, L, Hq, Hkv, d, G, shifted_heads,
+                    nullptr, nullptr, 0, stream, launch ? kStageAll : 0);
+}
+
 int attention_config_status(int is_bwd, int B, int L, int Hq, int Hkv, int d, int G,
                             int shifted_heads, const s2attn_opts* opts) {
     int st = check_sizes(B, L, Hq, Hkv, d, G, shifted_heads);

@@ -381,3 +381,23 @@ def test_block_binding_checks_shapes():
         blk.backward(_bf(1, 64, 64), params, saved, _bf(1, 64, 32))
     with pytest.raises(ValueError, match="lse"):
         blk.backward(_bf(1, 64, 64), params, dict(saved, lse=saved["lse"].bfloat16()), _bf(1, 64, 64))
+
+
+def test_noalloc_checks_run_on_the_host():
+    """s2attn_bwd_noalloc runs s2attn_bwd's argument checks, then its size
+    bound, before any HIP call."""
+    lib = L.lib()
+
+    def call(**kw):
+        a = dict(GOOD, **kw)
+        ptrs = [kw.get(n, FAKE) for n in ("q", "k", "v", "o", "lse", "do", "dq", "dk", "dv")]
+        return lib.s2attn_bwd_noalloc(*ptrs, a["B"], a["L"], a["Hq"], a["Hkv"], a["d"], a["G"],
+                                      a["sh"], None)
+    assert call(q=None) == INV
+    assert call(dv=MIS) == INV
+    assert call(G=100) == INV
+    assert call(d=80) == UNS
+    assert call(Hq=8, Hkv=2, sh=3) == UNS
+    # B Hq L = 2^24 row-term floats: past the library's array
+    assert call(B=2, L=1 << 22, Hq=2, Hkv=2, G=1 << 22, sh=0) == WS
+    assert L.S2ATTN_NOALLOC_MAX_ROWS == 1 << 23
