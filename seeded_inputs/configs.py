@@ -111,6 +111,10 @@ BLOCK_CONFIGS = {
         name="block_bf16_L1k", B=1, L=1024, Hq=4, Hkv=2, d=128, G=256, shifted_heads=2,
         lora_rank=8, lora_scale=2.0, seed=11, rope=True, rope_orig_len=256,
         note="small block: GQA, RoPE position interpolation 256 -> 1024"),
+    "block_bf16_L8k": BlockWorkload(
+        name="block_bf16_L8k", B=1, L=8192, Hq=32, Hkv=32, d=128, G=2048, shifted_heads=16,
+        lora_rank=8, lora_scale=2.0, seed=13, rope=True, rope_orig_len=4096,
+        note="Llama2-7B attention block at 8k (groups of L/4), RoPE position interpolation 4k -> 8k"),
     "block_bf16_L32k": BlockWorkload(
         name="block_bf16_L32k", B=1, L=32768, Hq=32, Hkv=32, d=128, G=8192, shifted_heads=16,
         lora_rank=8, lora_scale=2.0, seed=12, rope=True, rope_orig_len=4096,

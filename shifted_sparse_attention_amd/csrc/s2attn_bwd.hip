@@ -906,31 +906,44 @@ __global__ __launch_bounds__(64 * DQS_WAVES) void bwd_dq_ds_kernel(Params p, int
 }
 
 // ---------------------------------------------------------------------------
-// fp32 backward: one thread per row, plain FMA arithmetic.
-// dQ: thread per query, loop over its keys.  dK/dV: thread per key, loop
+// fp32 backward: plain FMA arithmetic, F32_TPR = D / 32 threads per row, each
+// holding 32 of its channels (a whole row per thread would need more
+// registers than a wave has at D = 128).  Dot products over the row add the
+// threads' partial sums with lane shuffles.
+// dQ: threads per query, loop over its keys.  dK/dV: threads per key, loop
 // over the query heads sharing the KV head and the queries at or after it.
 // ---------------------------------------------------------------------------
 constexpr int F32_ROWS = 64;
+constexpr int F32_CH = 32;   // channels per thread
+
+template <int TPR>
+__device__ __forceinline__ float row_sum(float x) {
+#pragma unroll
+    for (int off = TPR / 2; off > 0; off >>= 1) x += __shfl_xor(x, off, TPR);
+    return x;
+}
 
 template <int D>
-__global__ __launch_bounds__(F32_ROWS) void bwd_dq_f32_kernel(Params p, int n_qt) {
+__global__ __launch_bounds__(F32_ROWS * (D / F32_CH)) void bwd_dq_f32_kernel(Params p, int n_qt) {
+    constexpr int TPR = D / F32_CH;
     __shared__ float sK[F32_ROWS][D];
     __shared__ float sV[F32_ROWS][D];
     const int n_units = p.B * p.Hq * p.n_g;
     const Work w = decode_work(blockIdx.x, n_units, n_qt, p.Hq, p.n_g, p.band);
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, nthr = F32_ROWS * TPR;
+    const int rloc = tid / TPR, c0 = (tid % TPR) * F32_CH;
     const int s = head_shift(p, w.h);
     const int hk = w.h / p.r;
     const float* __restrict__ k = static_cast<const float*>(p.k);
     const float* __restrict__ v = static_cast<const float*>(p.v);
     const int q0 = w.tile * F32_ROWS;
-    const int qi = q0 + tid;
+    const int qi = q0 + rloc;
     const bool q_valid = qi < p.G;
     const int q_t = orig_row(w.g, p.G, q_valid ? qi : 0, s, p.L);
-    const size_t qo = q_row(p, w.b, q_t, w.h);
-    float qr[D], gr[D], acc[D];
+    const size_t qo = q_row(p, w.b, q_t, w.h) + c0;
+    float qr[F32_CH], gr[F32_CH], acc[F32_CH];
 #pragma unroll
-    for (int c = 0; c < D; ++c) {
+    for (int c = 0; c < F32_CH; ++c) {
         qr[c] = q_valid ? static_cast<const float*>(p.q)[qo + c] : 0.f;
         gr[c] = q_valid ? static_cast<const float*>(p.dout)[qo + c] : 0.f;
         acc[c] = 0.f;
@@ -941,7 +954,7 @@ __global__ __launch_bounds__(F32_ROWS) void bwd_dq_f32_kernel(Params p, int n_qt
     const int q_end = min(q0 + F32_ROWS, p.G);
     for (int k0 = 0; k0 < q_end; k0 += F32_ROWS) {
         __syncthreads();
-        for (int e = tid; e < F32_ROWS * D; e += F32_ROWS) {
+        for (int e = tid; e < F32_ROWS * D; e += nthr) {
             const int row = e / D, col = e % D, j = k0 + row;
             float kv = 0.f, vv = 0.f;
             if (j < p.G) {
@@ -953,29 +966,33 @@ __global__ __launch_bounds__(F32_ROWS) void bwd_dq_f32_kernel(Params p, int n_qt
             sV[row][col] = vv;
         }
         __syncthreads();
+        // keys k0 .. qi; the TPR threads of a row share the bound
         const int jmax = min(F32_ROWS, qi - k0 + 1);
         for (int j = 0; j < jmax; ++j) {
             float sd = 0.f, dp = 0.f;
 #pragma unroll
-            for (int c = 0; c < D; ++c) {
-                sd = fmaf(qr[c], sK[j][c], sd);
-                dp = fmaf(gr[c], sV[j][c], dp);
+            for (int c = 0; c < F32_CH; ++c) {
+                sd = fmaf(qr[c], sK[j][c0 + c], sd);
+                dp = fmaf(gr[c], sV[j][c0 + c], dp);
             }
+            sd = row_sum<TPR>(sd);
+            dp = row_sum<TPR>(dp);
             const float pv = expf(sd * p.scale - lse);
             const float ds = pv * (dp + dl) * p.scale;  // dl = -delta
 #pragma unroll
-            for (int c = 0; c < D; ++c) acc[c] = fmaf(ds, sK[j][c], acc[c]);
+            for (int c = 0; c < F32_CH; ++c) acc[c] = fmaf(ds, sK[j][c0 + c], acc[c]);
         }
     }
     if (q_valid) {
         float* dst = static_cast<float*>(p.dq) + qo;
 #pragma unroll
-        for (int c = 0; c < D; ++c) dst[c] = acc[c];
+        for (int c = 0; c < F32_CH; ++c) dst[c] = acc[c];
     }
 }
 
 template <int D>
-__global__ __launch_bounds__(F32_ROWS) void bwd_dkdv_f32_kernel(Params p, int n_kt) {
+__global__ __launch_bounds__(F32_ROWS * (D / F32_CH)) void bwd_dkdv_f32_kernel(Params p, int n_kt) {
+    constexpr int TPR = D / F32_CH;
     __shared__ float sQ[F32_ROWS][D];
     __shared__ float sG[F32_ROWS][D];
     __shared__ float sL[F32_ROWS], sD[F32_ROWS];
@@ -983,16 +1000,17 @@ __global__ __launch_bounds__(F32_ROWS) void bwd_dkdv_f32_kernel(Params p, int n_
     Work w = decode_work(blockIdx.x, n_units, n_kt, p.Hkv, p.n_g, p.band);
     w.tile = n_kt - 1 - w.tile;
     const int hk = w.h;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, nthr = F32_ROWS * TPR;
+    const int rloc = tid / TPR, c0 = (tid % TPR) * F32_CH;
     const int s = head_shift(p, hk * p.r);
     const int k0 = w.tile * F32_ROWS;
-    const int kj = k0 + tid;
+    const int kj = k0 + rloc;
     const bool k_valid = kj < p.G;
     const int k_t = orig_row(w.g, p.G, k_valid ? kj : 0, s, p.L);
-    const size_t ko = kv_row(p, w.b, k_t, hk);
-    float kr[D], vr[D], dk[D], dv[D];
+    const size_t ko = kv_row(p, w.b, k_t, hk) + c0;
+    float kr[F32_CH], vr[F32_CH], dk[F32_CH], dv[F32_CH];
 #pragma unroll
-    for (int c = 0; c < D; ++c) {
+    for (int c = 0; c < F32_CH; ++c) {
         kr[c] = k_valid ? static_cast<const float*>(p.k)[ko + c] : 0.f;
         vr[c] = k_valid ? static_cast<const float*>(p.v)[ko + c] : 0.f;
         dk[c] = 0.f;
@@ -1002,7 +1020,7 @@ __global__ __launch_bounds__(F32_ROWS) void bwd_dkdv_f32_kernel(Params p, int n_
         const int h = hk * p.r + hr;
         for (int q0 = k0; q0 < p.G; q0 += F32_ROWS) {
             __syncthreads();
-            for (int e = tid; e < F32_ROWS * D; e += F32_ROWS) {
+            for (int e = tid; e < F32_ROWS * D; e += nthr) {
                 const int row = e / D, col = e % D, i = q0 + row;
                 float a = 0.f, b = 0.f;
                 if (i < p.G) {
@@ -1013,7 +1031,7 @@ __global__ __launch_bounds__(F32_ROWS) void bwd_dkdv_f32_kernel(Params p, int n_
                 sQ[row][col] = a;
                 sG[row][col] = b;
             }
-            {
+            if (tid < F32_ROWS) {
                 const int i = q0 + tid;
                 float l = INFINITY, dl = 0.f;
                 if (i < p.G) {
@@ -1025,20 +1043,23 @@ __global__ __launch_bounds__(F32_ROWS) void bwd_dkdv_f32_kernel(Params p, int n_
                 sD[tid] = dl;
             }
             __syncthreads();
-            for (int i = 0; i < F32_ROWS; ++i) {
-                if (q0 + i < kj) continue;  // causal: queries at or after the key
+            // causal: queries at or after the key (shared by a row's threads)
+            const int i0 = max(0, kj - q0);
+            for (int i = i0; i < F32_ROWS; ++i) {
                 float sd = 0.f, dp = 0.f;
 #pragma unroll
-                for (int c = 0; c < D; ++c) {
-                    sd = fmaf(sQ[i][c], kr[c], sd);
-                    dp = fmaf(sG[i][c], vr[c], dp);
+                for (int c = 0; c < F32_CH; ++c) {
+                    sd = fmaf(sQ[i][c0 + c], kr[c], sd);
+                    dp = fmaf(sG[i][c0 + c], vr[c], dp);
                 }
+                sd = row_sum<TPR>(sd);
+                dp = row_sum<TPR>(dp);
                 const float pv = expf(sd * p.scale - sL[i]);
                 const float ds = pv * (dp + sD[i]) * p.scale;  // sD = -delta
 #pragma unroll
-                for (int c = 0; c < D; ++c) {
-                    dv[c] = fmaf(pv, sG[i][c], dv[c]);
-                    dk[c] = fmaf(ds, sQ[i][c], dk[c]);
+                for (int c = 0; c < F32_CH; ++c) {
+                    dv[c] = fmaf(pv, sG[i][c0 + c], dv[c]);
+                    dk[c] = fmaf(ds, sQ[i][c0 + c], dk[c]);
                 }
             }
         }
@@ -1047,7 +1068,7 @@ __global__ __launch_bounds__(F32_ROWS) void bwd_dkdv_f32_kernel(Params p, int n_
         float* a = static_cast<float*>(p.dk) + ko;
         float* b = static_cast<float*>(p.dv) + ko;
 #pragma unroll
-        for (int c = 0; c < D; ++c) {
+        for (int c = 0; c < F32_CH; ++c) {
             a[c] = dk[c];
             b[c] = dv[c];
         }
@@ -1151,9 +1172,11 @@ hipError_t launch_bwd_dkdv_f32(const Params& p, hipStream_t st) {
     const int n_kt = (p.G + F32_ROWS - 1) / F32_ROWS;
     const long blocks = (long)p.B * p.Hkv * p.n_g * n_kt;
     if (p.d == 128)
-        hipLaunchKernelGGL(bwd_dkdv_f32_kernel<128>, dim3(blocks), dim3(F32_ROWS), 0, st, p, n_kt);
+        hipLaunchKernelGGL(bwd_dkdv_f32_kernel<128>, dim3(blocks), dim3(F32_ROWS * 128 / F32_CH), 0,
+                           st, p, n_kt);
     else
-        hipLaunchKernelGGL(bwd_dkdv_f32_kernel<64>, dim3(blocks), dim3(F32_ROWS), 0, st, p, n_kt);
+        hipLaunchKernelGGL(bwd_dkdv_f32_kernel<64>, dim3(blocks), dim3(F32_ROWS * 64 / F32_CH), 0,
+                           st, p, n_kt);
     return hipGetLastError();
 }
 
@@ -1161,9 +1184,11 @@ hipError_t launch_bwd_dq_f32(const Params& p, hipStream_t st) {
     const int n_qt = (p.G + F32_ROWS - 1) / F32_ROWS;
     const long blocks = (long)p.B * p.Hq * p.n_g * n_qt;
     if (p.d == 128)
-        hipLaunchKernelGGL(bwd_dq_f32_kernel<128>, dim3(blocks), dim3(F32_ROWS), 0, st, p, n_qt);
+        hipLaunchKernelGGL(bwd_dq_f32_kernel<128>, dim3(blocks), dim3(F32_ROWS * 128 / F32_CH), 0,
+                           st, p, n_qt);
     else
-        hipLaunchKernelGGL(bwd_dq_f32_kernel<64>, dim3(blocks), dim3(F32_ROWS), 0, st, p, n_qt);
+        hipLaunchKernelGGL(bwd_dq_f32_kernel<64>, dim3(blocks), dim3(F32_ROWS * 64 / F32_CH), 0,
+                           st, p, n_qt);
     return hipGetLastError();
 }
 

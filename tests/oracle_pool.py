@@ -94,3 +94,36 @@ def full_backward(x, G, shifted_heads, rope=None):
         dk[b, rows, hk] = u["dk"]
         dv[b, rows, hk] = u["dv"]
     return o, lse, dq, dk, dv
+
+
+def _fwd_task(args):
+    key, qg, kg, vg, scale = args
+    return key, O.unit_forward(qg, kg, vg, scale)
+
+
+def full_forward(q, k, v, G, shifted_heads, rope=None, scale=None):
+    """Whole (o, lse) in float64 from every (b, h, g) unit's `unit_forward`,
+    q and k rotated first (oracle.s2attn.rope_rotate) when `rope` is given."""
+    B, L, Hq, d = q.shape
+    r = Hq // k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    theta = O.rope_angles(L, d, *rope) if rope is not None else None
+    rows_of, tasks = {}, []
+    for b, h, g in O.units(B, Hq, L, G):
+        rows = O.unit_rows(L, G, Hq, shifted_heads, h, g)
+        qg = np.asarray(q[b, rows, h], dtype=np.float64)
+        kg = np.asarray(k[b, rows, h // r], dtype=np.float64)
+        if theta is not None:
+            qg = O.rope_rotate(qg[None, :, None, :], theta[rows])[0, :, 0, :]
+            kg = O.rope_rotate(kg[None, :, None, :], theta[rows])[0, :, 0, :]
+        rows_of[(b, h, g)] = rows
+        tasks.append(((b, h, g), qg, kg, np.asarray(v[b, rows, h // r], dtype=np.float64), scale))
+    pool = _POOL if _POOL is not None else start()
+    o = np.empty((B, L, Hq, d))
+    lse = np.empty((B, Hq, L))
+    for (b, h, g), (og, lg) in pool.imap_unordered(_fwd_task, tasks):
+        rows = rows_of[(b, h, g)]
+        o[b, rows, h] = og
+        lse[b, h, rows] = lg
+    return o, lse

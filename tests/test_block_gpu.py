@@ -83,10 +83,34 @@ def test_block_small_variants(sh, rank):
         _check("db" + n, host(g["db" + n]), rg["db" + n])
 
 
+@pytest.mark.timeout(600)
+def test_block_llama7b_8k_whole_tensors():
+    """The Llama2-7B block (32 heads, d = 128, hidden 4096, LoRA rank 8) at
+    8k tokens with RoPE-PI 4k -> 8k and groups of 2048: y, dx and every
+    LoRA gradient over whole tensors against the block oracle."""
+    wl = BLOCK_CONFIGS["block_bf16_L8k"]
+    say(f"[block] {wl.name}, whole tensors")
+    inp = make_block_inputs(wl)
+    _, _, _, y, _, g = _run(wl, inp)
+    rope = (wl.rope_base, wl.rope_orig_len)
+    say("  block oracle (fp64)")
+    ry, rg = OB.backward(inp["x"], inp["params"], inp["dy"], wl.G, wl.shifted_heads, wl.Hq,
+                         wl.Hkv, wl.d, wl.lora_scale, rope=rope)
+    _check("y", host(y), ry)
+    _check("dx", host(g["dx"]), rg["dx"])
+    for n in ("q", "k", "v", "o"):
+        _check("da" + n, host(g["da" + n]), rg["da" + n])
+        _check("db" + n, host(g["db" + n]), rg["db" + n])
+
+
+@pytest.mark.timeout(600)
 def test_block_llama7b_32k():
-    """The Llama2-7B block at 32k: y at sampled tokens against the oracle
-    (token by token), and the O-projection LoRA gradients against fp32
-    products of the saved activations."""
+    """The Llama2-7B block at 32k: y over the whole tensor and the
+    O-projection LoRA gradients (sums over all 32768 rows) against the block
+    oracle's projections around the attention oracle's output, computed in
+    worker processes over every (head, group) unit; y at sampled tokens also
+    against the token-by-token oracle; every output finite."""
+    from tests import oracle_pool
     wl = BLOCK_CONFIGS["block_bf16_L32k"]
     say(f"[block] {wl.name}")
     inp = make_block_inputs(wl)
@@ -96,17 +120,23 @@ def test_block_llama7b_32k():
     G, L = wl.G, wl.L
     toks = [0, 1, G // 2 - 1, G // 2, G - 1, G, 2 * G + 17, L - G // 2, L - 1]
     rope = (wl.rope_base, wl.rope_orig_len)
-    ry = OB.sampled_forward_tokens(inp["x"], inp["params"], G, wl.shifted_heads, wl.Hq, wl.Hkv,
-                                   wl.d, wl.lora_scale, 0, toks, rope=rope)
-    _check("y[sampled tokens]", host(y[0, toks]), ry)
-    # dBo = s dy^T (attn Ao^T), dAo = s (dy Bo)^T attn, in fp32 from the saved
-    # tensors (the saved u holds s attn Ao^T)
-    s, r = wl.lora_scale, wl.lora_rank
-    M = wl.B * wl.L
-    dyf = dy.reshape(M, -1).float()
-    attn = saved["attn"].reshape(M, -1).float()
-    u_o = saved["u"][:, 3 * r:4 * r].float()
-    ref_dbo = dyf.t() @ u_o
-    ref_dao = s * ((dyf @ params["bo"].float()).t() @ attn)
-    _check("dbo (vs fp32 product)", host(g["dbo"]), host(ref_dbo))
-    _check("dao (vs fp32 product)", host(g["dao"]), host(ref_dao))
+    ry_tok = OB.sampled_forward_tokens(inp["x"], inp["params"], G, wl.shifted_heads, wl.Hq,
+                                       wl.Hkv, wl.d, wl.lora_scale, 0, toks, rope=rope)
+    _check("y[sampled tokens]", host(y[0, toks]), ry_tok)
+    say("  oracle projections (fp64) and attention over every unit")
+    p, s = inp["params"], wl.lora_scale
+    M, Dm = wl.B * L, wl.Hq * wl.d
+    X = inp["x"].reshape(M, Dm)
+    q = OB.lora_proj(X, p["wq"], p["aq"], p["bq"], s).reshape(wl.B, L, wl.Hq, wl.d)
+    k = OB.lora_proj(X, p["wk"], p["ak"], p["bk"], s).reshape(wl.B, L, wl.Hkv, wl.d)
+    v = OB.lora_proj(X, p["wv"], p["av"], p["bv"], s).reshape(wl.B, L, wl.Hkv, wl.d)
+    attn, _ = oracle_pool.full_forward(q, k, v, G, wl.shifted_heads, rope)
+    del q, k, v
+    attn = attn.reshape(M, Dm)
+    ry = OB.lora_proj(attn, p["wo"], p["ao"], p["bo"], s)
+    _check("y", host(y).reshape(M, Dm), ry)
+    del ry
+    _, rdao, rdbo = OB.lora_proj_backward(attn, p["wo"], p["ao"], p["bo"], s,
+                                          inp["dy"].reshape(M, Dm))
+    _check("dao", host(g["dao"]), rdao)
+    _check("dbo", host(g["dbo"]), rdbo)

@@ -444,8 +444,9 @@ def test_invalid_arguments():
 def test_pooled_units_equal_the_oracle():
     """The worker-pool driver the full-size GPU parity tests use returns the
     oracle's own values: every KV unit through `kv_unit_backward` in worker
-    processes, scattered back, equals `backward` bit for bit (GQA, shifted
-    heads, B = 2, with and without RoPE)."""
+    processes, scattered back, equals `backward` bit for bit, and every unit
+    through `unit_forward` equals `forward` (GQA, shifted heads, B = 2, with
+    and without RoPE)."""
     from tests import oracle_pool
     rng = np.random.default_rng(12)
     B, L, Hq, Hkv, d, G, sh = 2, 192, 4, 2, 16, 48, 2
@@ -458,6 +459,9 @@ def test_pooled_units_equal_the_oracle():
             po, plse, pdq, pdk, pdv = oracle_pool.full_backward(x, G, sh, rope)
             for a, b in ((po, o), (plse, lse), (pdq, dq), (pdk, dk), (pdv, dv)):
                 assert np.array_equal(a, b)
+            fo, flse = oracle_pool.full_forward(x["q"], x["k"], x["v"], G, sh, rope)
+            ro, rlse = O.forward(x["q"], x["k"], x["v"], G, sh, rope=rope)
+            assert np.array_equal(fo, ro) and np.array_equal(flse, rlse)
     finally:
         if started_here:
             oracle_pool.stop()
