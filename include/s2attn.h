@@ -172,6 +172,9 @@ int s2attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* 
  * (0 when none).  is_bwd selects the backward.  Returns 0 for invalid
  * arguments as well; the _ex call then reports the error.
  *
+ * Forward workspace: with RoPE the rotated k (bf16, the size of k); the
+ * kernel rotates its own query tile in registers.  None without RoPE.
+ *
  * Backward workspace, each part 256-byte aligned: the row term -delta
  * (B Hq L floats); with RoPE the rotated q and k (bf16, the sizes of q and
  * k); for bf16 inputs, the dS tiles: per (batch, head, group) the 32 x 32

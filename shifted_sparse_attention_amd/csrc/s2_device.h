@@ -208,4 +208,32 @@ __device__ __forceinline__ Work decode_work(int bid, int n_units, int n_tiles, i
     return w;
 }
 
+// ---------------------------------------------------------------------------
+// RoPE with position interpolation (LongLoRA blog, section 3.4): channel pair
+// (c, c + d/2) of original position t turns by t * (L0/L) * base^(-2c/d).
+// The angle is formed in revolutions in double precision and reduced to
+// [-1/2, 1/2] there, so the hardware sine / cosine (which take revolutions)
+// see a small argument whatever the position.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void rope_cs(const Params& p, int t, int c, float* cs, float* sn) {
+    double r = (double)t * p.rope_rev[c];
+    r -= rint(r);
+    const float x = (float)r;
+    *sn = __builtin_amdgcn_sinf(x);
+    *cs = __builtin_amdgcn_cosf(x);
+}
+
+// One channel pair of a bf16 row turned by the angle of (t, c), rounded to
+// bf16.  The pre-pass and the forward's query fragments both call this, so a
+// rotated operand is the same value whichever of them formed it.
+struct BfPair {
+    bf16 a, b;
+};
+__device__ __forceinline__ BfPair rope_turn(const Params& p, int t, int c, bf16 a, bf16 b) {
+    float cs, sn;
+    rope_cs(p, t, c, &cs, &sn);
+    const float x1 = (float)a, x2 = (float)b;
+    return {(bf16)fmaf(x1, cs, -(x2 * sn)), (bf16)fmaf(x1, sn, x2 * cs)};
+}
+
 }  // namespace s2

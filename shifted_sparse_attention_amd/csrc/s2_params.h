@@ -41,7 +41,9 @@ struct Params {
     float scale_log2;  // scale * log2(e)
     // RoPE with position interpolation: angle = t * pos_scale * rope_base^(-2c/d), with
     // pos_scale = L0 / L.  rope_rev[c] is that angle per unit of t, in revolutions
-    // (divided by 2 pi), formed in double precision on the host.
+    // (divided by 2 pi), formed in double precision on the host.  With rope set,
+    // the bf16 forward rotates its query fragments (k comes pre-rotated) and the
+    // backward epilogues rotate dq, dk back (q and k come pre-rotated).
     int rope;
     double rope_rev[64];
     // Units per dispatch band of the tiled kernels (see decode_work; >= 1).
@@ -87,6 +89,7 @@ hipError_t launch_bwd_dq_bf16(const Params& p, int grad_f32, hipStream_t s);
 hipError_t launch_bwd_dq_ds_bf16(const Params& p, int grad_f32, hipStream_t s);
 hipError_t launch_bwd_dkdv_f32(const Params& p, hipStream_t s);
 hipError_t launch_bwd_dq_f32(const Params& p, hipStream_t s);
+// Rotated q into q_out (skipped when q_out is null) and rotated k into k_out.
 hipError_t launch_rope_prepass(const Params& p, void* q_out, void* k_out, hipStream_t s);
 
 // The plain backward (s2attn_bwd) with the row term in `delta`; with launch = 0

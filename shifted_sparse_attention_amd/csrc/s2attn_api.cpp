@@ -130,9 +130,13 @@ WsLayout ws_layout(int is_bwd, int B, int L, int Hq, int Hkv, int d, int G, cons
         off += align_up(w.delta_bytes);
     }
     if (r.rope) {
-        w.rq_off = off;
-        w.rq_bytes = (size_t)B * L * Hq * d * 2;
-        off += align_up(w.rq_bytes);
+        // The forward rotates its stationary query tile in registers; only the
+        // backward (which streams q) keeps a rotated copy of q.
+        if (is_bwd) {
+            w.rq_off = off;
+            w.rq_bytes = (size_t)B * L * Hq * d * 2;
+            off += align_up(w.rq_bytes);
+        }
         w.rk_off = off;
         w.rk_bytes = (size_t)B * L * Hkv * d * 2;
         off += align_up(w.rk_bytes);
@@ -198,14 +202,12 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
     p.lse = lse;
     if (r.dtype == S2ATTN_F32) return hip_status(s2::launch_fwd_f32(p, stream));
     if (r.rope) {
-        char* base = static_cast<char*>(ws);
-        void* rq = base + wl.rq_off;
-        void* rk = base + wl.rk_off;
-        hipError_t e = s2::launch_rope_prepass(p, rq, rk, stream);
+        // k is streamed by every query tile, so it is rotated once by the
+        // pre-pass; the kernel rotates its query fragments itself (p.rope).
+        void* rk = static_cast<char*>(ws) + wl.rk_off;
+        hipError_t e = s2::launch_rope_prepass(p, nullptr, rk, stream);
         if (e != hipSuccess) return S2ATTN_ERR_HIP;
-        p.q = rq;
         p.k = rk;
-        p.rope = 0;  // the forward's outputs need no rotation back
     }
     return hip_status(s2::launch_fwd_bf16(p, stream));
 }

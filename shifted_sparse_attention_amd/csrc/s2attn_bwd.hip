@@ -56,22 +56,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(Params p, long n_rows) {
     }
 }
 
-// ---------------------------------------------------------------------------
-// RoPE with position interpolation (LongLoRA blog, section 3.4): channel pair
-// (c, c + d/2) of original position t turns by t * (L0/L) * base^(-2c/d).
-// The angle is formed in revolutions in double precision and reduced to
-// [-1/2, 1/2] there, so the hardware sine / cosine (which take revolutions)
-// see a small argument whatever the position.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ void rope_cs(const Params& p, int t, int c, float* cs, float* sn) {
-    double r = (double)t * p.rope_rev[c];
-    r -= rint(r);
-    const float x = (float)r;
-    *sn = __builtin_amdgcn_sinf(x);
-    *cs = __builtin_amdgcn_cosf(x);
-}
-
-// Rotated copies of q and k (bf16 in, bf16 out).  A thread turns 8 channel
+// Rotated copies of q (when qo is set) and k (bf16 in, bf16 out).  A thread turns 8 channel
 // pairs: 16 bytes from each half of the row in, 16 bytes to each half out.
 template <int D>
 __global__ __launch_bounds__(256) void rope_prepass_kernel(Params p, bf16* qo, bf16* ko,
@@ -93,11 +78,9 @@ __global__ __launch_bounds__(256) void rope_prepass_kernel(Params p, bf16* qo, b
     bf16x8 oa, ob;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        float cs, sn;
-        rope_cs(p, t, c0 + i, &cs, &sn);
-        const float x1 = (float)a[i], x2 = (float)b[i];
-        oa[i] = (bf16)(x1 * cs - x2 * sn);
-        ob[i] = (bf16)(x1 * sn + x2 * cs);
+        const BfPair r2 = rope_turn(p, t, c0 + i, a[i], b[i]);
+        oa[i] = r2.a;
+        ob[i] = r2.b;
     }
     *reinterpret_cast<bf16x8*>(dst) = oa;
     *reinterpret_cast<bf16x8*>(dst + HALF) = ob;
@@ -1097,7 +1080,7 @@ hipError_t launch_bwd_pre(const Params& p, int f32_io, hipStream_t st) {
 }
 
 hipError_t launch_rope_prepass(const Params& p, void* q_out, void* k_out, hipStream_t st) {
-    const long q_rows = (long)p.B * p.L * p.Hq, k_rows = (long)p.B * p.L * p.Hkv;
+    const long q_rows = q_out ? (long)p.B * p.L * p.Hq : 0, k_rows = (long)p.B * p.L * p.Hkv;
     const long threads = (q_rows + k_rows) * (p.d / 16);  // 8 channel pairs per thread
     const long blocks = (threads + 255) / 256;
     if (p.d == 128)

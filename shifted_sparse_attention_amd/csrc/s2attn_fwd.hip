@@ -29,7 +29,8 @@ constexpr int FWD_BM = 32 * FWD_WAVES;
 constexpr int FWD_BN = 128;
 constexpr int FWD_THREADS = 64 * FWD_WAVES;
 
-template <int D>
+// ROPE: rotate the query fragments after loading them (k arrives rotated).
+template <int D, bool ROPE>
 __global__ __launch_bounds__(FWD_THREADS) void fwd_bf16_kernel(Params p, int n_qt) {
     constexpr int KS = D / 16;  // MFMA k-steps over the head dimension
     constexpr int CB = D / 32;  // 32-channel blocks of the output
@@ -112,6 +113,19 @@ __global__ __launch_bounds__(FWD_THREADS) void fwd_bf16_kernel(Params p, int n_q
         for (int ks = 0; ks < KS; ++ks) {
             u32x4 raw = q_valid ? ld_global16(qr + 16 * ks) : u32x4{0, 0, 0, 0};
             qf[ks] = __builtin_bit_cast(bf16x8, raw);
+        }
+        // RoPE on the stationary query: fragment ks holds channels
+        // 16 ks + 8 hh + i, and its pair partner (+ D/2) sits in fragment
+        // ks + KS/2 of the same lane, so the rotation stays in registers.
+        if constexpr (ROPE) {
+#pragma unroll
+            for (int ks = 0; ks < KS / 2; ++ks)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const BfPair r2 = rope_turn(p, q_t, 16 * ks + 8 * hh + i, qf[ks][i], qf[ks + KS / 2][i]);
+                    qf[ks][i] = r2.a;
+                    qf[ks + KS / 2][i] = r2.b;
+                }
         }
     }
 
@@ -332,10 +346,9 @@ hipError_t launch_fwd_bf16(const Params& p0, hipStream_t st) {
     const long blocks = (long)p0.B * p0.Hq * p0.n_g * n_qt;
     Params p = p0;
     p.band = dispatch_band(p.B * p.Hq * p.n_g, (size_t)p.G * p.d * 4);  // K and V of the unit
-    if (p.d == 128)
-        hipLaunchKernelGGL(fwd_bf16_kernel<128>, dim3(blocks), dim3(FWD_THREADS), 0, st, p, n_qt);
-    else
-        hipLaunchKernelGGL(fwd_bf16_kernel<64>, dim3(blocks), dim3(FWD_THREADS), 0, st, p, n_qt);
+    auto kernel = p.d == 128 ? (p.rope ? fwd_bf16_kernel<128, true> : fwd_bf16_kernel<128, false>)
+                             : (p.rope ? fwd_bf16_kernel<64, true> : fwd_bf16_kernel<64, false>);
+    hipLaunchKernelGGL(kernel, dim3(blocks), dim3(FWD_THREADS), 0, st, p, n_qt);
     return hipGetLastError();
 }
 

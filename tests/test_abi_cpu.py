@@ -184,7 +184,8 @@ def test_workspace_sizes_and_checks():
     assert s2.s2attn_workspace_size(1, B, 240, Hq, Hkv, d, Gr, o) == r256(B * Hq * 240 * 4) + r256(dsr)
     o.rope = 1
     rq, rk = B * Ln * Hq * d * 2, B * Ln * Hkv * d * 2
-    assert s2.s2attn_workspace_size(0, B, Ln, Hq, Hkv, d, G, o) == r256(rq) + r256(rk)
+    # the forward rotates its stationary query tile in registers: only k~ is kept
+    assert s2.s2attn_workspace_size(0, B, Ln, Hq, Hkv, d, G, o) == r256(rk)
     assert s2.s2attn_workspace_size(1, B, Ln, Hq, Hkv, d, G, o) == (
         r256(delta) + r256(rq) + r256(rk) + r256(ds))
     assert s2.s2attn_workspace_size(0, 0, Ln, Hq, Hkv, d, G, o) == 0   # invalid sizes -> 0
