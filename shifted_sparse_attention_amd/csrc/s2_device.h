@@ -216,8 +216,10 @@ __device__ __forceinline__ Work decode_work(int bid, int n_units, int n_tiles, i
 // see a small argument whatever the position.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void rope_cs(const Params& p, int t, int c, float* cs, float* sn) {
-    double r = (double)t * p.rope_rev[c];
-    r -= rint(r);
+    // t * w less its nearest integer, with the product unrounded (one FMA), so
+    // every kernel that calls this forms the same angle.
+    const double tt = (double)t, w = p.rope_rev[c];
+    const double r = fma(tt, w, -rint(tt * w));
     const float x = (float)r;
     *sn = __builtin_amdgcn_sinf(x);
     *cs = __builtin_amdgcn_cosf(x);

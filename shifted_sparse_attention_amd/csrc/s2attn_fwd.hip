@@ -247,7 +247,7 @@ __global__ __launch_bounds__(FWD_THREADS) void fwd_bf16_kernel(Params p, int n_q
         }
     }
     if (q_valid && hh == 0)
-        p.lse[lse_idx(p, w.b, w.h, orig_row(w.g, p.G, qi, s, p.L))] = m * p.scale + log2f(l_tot) * kLn2;
+        p.lse[lse_idx(p, w.b, w.h, orig_row(w.g, p.G, qi, s, p.L))] = fmaf(m, p.scale, log2f(l_tot) * kLn2);
     __syncthreads();
     constexpr int LPR = D / 8;
     bf16* o = static_cast<bf16*>(p.o);

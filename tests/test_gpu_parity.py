@@ -671,6 +671,41 @@ def test_backward_stages_on_two_streams_without_ds(rope):
         assert torch.equal(a, want), name
 
 
+@pytest.mark.parametrize("d,Hkv", [(128, 2), (64, 4)])
+def test_fused_query_rotation_equals_the_prepass(d, Hkv):
+    """With RoPE the forward rotates its query fragments in registers, while the
+    backward's pre-pass writes rotated q~ and k~ to its workspace (after the row
+    term, each part 256-byte aligned, as the header lays it out).  Both call one
+    rotation, so a forward without RoPE on those q~ and k~ reproduces the fused
+    forward's o and lse bit for bit (rows of wrapped, shifted and ragged groups
+    included: L = 600, G = 200)."""
+    B, L, Hq, G, sh = 1, 600, 4, 200, 2
+    rope = (10000.0, 64)
+    say(f"[fused rotation] d={d} Hkv={Hkv}")
+    q, k, v, do = rand_inputs(47, B, L, Hq, Hkv, d)
+    tq, tk, tv, tdo = (dev(x, BF) for x in (q, k, v, do))
+    o, lse = s2.forward(tq, tk, tv, G, sh, rope=rope)
+    opts = s2.make_opts(BF, rope=rope)
+    n = s2.s2attn_workspace_size(1, B, L, Hq, Hkv, d, G, opts)
+    ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    dq, dk, dv = (torch.empty_like(x) for x in (tq, tk, tv))
+    s2.s2attn_bwd_stage_ex(s2.S2ATTN_BWD_STAGE_PRE, tq, tk, tv, o, lse, tdo, dq, dk, dv,
+                           B, L, Hq, Hkv, d, G, sh, opts, ws, n)
+    torch.cuda.synchronize()
+    r256 = lambda x: (x + 255) // 256 * 256
+    nq, nk = B * L * Hq * d * 2, B * L * Hkv * d * 2
+    off_q = r256(B * Hq * L * 4)
+    off_k = off_q + r256(nq)
+    assert off_k + nk <= n
+    qr = ws[off_q:off_q + nq].view(BF).view(B, L, Hq, d).clone()
+    kr = ws[off_k:off_k + nk].view(BF).view(B, L, Hkv, d).clone()
+    assert not torch.equal(qr, tq) and not torch.equal(kr, tk)   # rotated
+    o2, lse2 = s2.forward(qr, kr, tv, G, sh)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2)
+    assert torch.equal(lse, lse2)
+
+
 def test_graph_capture_replays_bitwise():
     """The forward and backward enqueue only kernel launches on the caller's
     stream (no allocation, copy, memset or synchronisation), so a caller can
