@@ -83,6 +83,65 @@ def test_small_bf16_fwd_bwd(case):
         check(name + "(bf16)", host(b), ref, BF16_REL_F, bf16_store_tol(ref))
 
 
+def _random_cases(n, seed):
+    """Seeded small shapes over the library's options: batch, query and KV
+    heads (GQA ratio 1, 2 or 4), d = 64 or 128, group sizes with ragged 32-
+    and 64-row tiles, 1-4 groups per sequence, shifted-head counts the
+    backward accepts (a multiple of Hq / Hkv; G even when any head shifts),
+    RoPE on or off, a softmax scale of its own, dS kept or recomputed, and
+    fp32- or bf16-stored gradients."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        d = int(rng.choice([64, 128]))
+        r = int(rng.choice([1, 2, 4]))
+        Hkv = int(rng.integers(1, 3))
+        Hq = Hkv * r
+        sh = r * int(rng.integers(0, Hkv + 1))
+        G = int(rng.integers(1, 700))
+        if sh and G % 2:
+            G += 1
+        n_g = int(rng.integers(1, 5))
+        L = G * n_g
+        if L > 2048:
+            continue
+        B = int(rng.integers(1, 3))
+        rope = (float(rng.choice([500.0, 10000.0])), int(rng.choice([64, 256]))) if rng.random() < 0.3 else None
+        scale = float(rng.uniform(0.05, 0.15)) if rng.random() < 0.25 else None
+        ds = 0 if rng.random() < 0.3 else None
+        gd = torch.float32 if rng.random() < 0.5 else BF
+        cases.append((B, L, Hq, Hkv, d, G, sh, rope, scale, ds, gd))
+    return cases
+
+
+RANDOM = _random_cases(64, 20261203)
+
+
+@pytest.mark.parametrize("case", RANDOM, ids=[
+    f"B{c[0]}L{c[1]}H{c[2]}/{c[3]}d{c[4]}G{c[5]}s{c[6]}{'rope' if c[7] else ''}"
+    f"{'scale' if c[8] else ''}{'ds0' if c[9] == 0 else ''}{'f32' if c[10] == torch.float32 else 'bf16'}"
+    for c in RANDOM])
+def test_random_small_shapes(case):
+    """Whole tensors against the oracle over a seeded sweep of shapes and
+    options, at the same bounds as the fixed small cases (fp32-stored
+    gradients and O at 2e-2 flat; bf16-stored gradients plus their store's
+    half ulp)."""
+    B, L, Hq, Hkv, d, G, sh, rope, scale, ds, gd = case
+    say(f"[random small] {case}")
+    q, k, v, do = rand_inputs(3000 + L + G + d, B, L, Hq, Hkv, d)
+    tq, tk, tv, tdo = (dev(x, BF) for x in (q, k, v, do))
+    o, lse = s2.forward(tq, tk, tv, G, sh, scale=scale, rope=rope)
+    g = s2.backward(tq, tk, tv, o, lse, tdo, G, sh, scale=scale, rope=rope, grad_dtype=gd,
+                    ds_max_mib=ds)
+    torch.cuda.synchronize()
+    rdq, rdk, rdv, ro, rlse = O.backward(q, k, v, do, G, sh, scale=scale, rope=rope)
+    check("o", host(o), ro, BF16_REL_F, BF16_MAX_ABS)
+    check("lse", host(lse), rlse, BF16_REL_F, BF16_MAX_ABS)
+    for name, a, ref in zip(("dq", "dk", "dv"), g, (rdq, rdk, rdv)):
+        tol = BF16_MAX_ABS if gd == torch.float32 else bf16_store_tol(ref)
+        check(name, host(a), ref, BF16_REL_F, tol)
+
+
 F32_CASES = [
     (1, 256, 4, 2, 64, 64, 2),
     (1, 192, 2, 2, 128, 96, 1),
