@@ -71,6 +71,13 @@ def kv_units(x, G, shifted_heads, units, rope=None, scale=None):
     return out
 
 
+def kv_units_gathered(tasks):
+    """{key: kv_unit_backward result} for tasks already gathered by the caller:
+    (key, qs [r, G, d], kg [G, d], vg [G, d], dos [r, G, d], scale, theta)."""
+    pool = _POOL if _POOL is not None else start()
+    return dict(pool.imap_unordered(_task, tasks))
+
+
 def full_backward(x, G, shifted_heads, rope=None):
     """Whole reference tensors (o, lse, dq, dk, dv) in float64 from every KV unit."""
     q, k = x["q"], x["k"]

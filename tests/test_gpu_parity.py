@@ -432,6 +432,58 @@ def _causal_rows(G):
     return sorted(edges | {G // 2 - 1, G // 2, G - 257, G - 256, G - 129, G - 128, G - 2, G - 1})
 
 
+@pytest.mark.timeout(600)
+def test_plane_at_the_32bit_offset_limit():
+    """The kernels address a tile row as a (batch, head) plane base plus a
+    32-bit byte offset, so the host accepts planes L H d 2 below 2^31 bytes.
+    Here a plane is 2^31 - 2^24 bytes: L = 520192, 16 heads, d = 128, G = 4096,
+    the longest L the host accepts at this head count and group size (one
+    more group reaches 2^31), with half the heads shifted.  The dS tiles are
+    kept (about 36 GB of workspace, past 2^32 bytes), and the fp32 gradients
+    are 4.3 GB per tensor.  The inputs are standard normals rounded to bf16,
+    drawn on the device by a seeded torch generator (no period, so an offset
+    that wrapped would read different values).  Units with rows at the
+    plane's far end, the wrap group of a shifted head (rows at both ends)
+    and the first and a middle unit match the oracle, rows gathered with the
+    oracle's own row map."""
+    import math
+    from tests import oracle_pool
+    B, L, Hq, Hkv, d, G, sh = 1, 520192, 16, 16, 128, 4096, 8
+    assert L * Hq * d * 2 == 2**31 - 2**24 and (L + G) * Hq * d * 2 == 2**31
+    say("[plane limit] L=520192 H=16 d=128 G=4096")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(52)
+    tq, tk, tv, tdo = (torch.randn((B, L, H, d), generator=gen, device="cuda").to(BF)
+                       for H in (Hq, Hkv, Hkv, Hq))
+    ds_mib = 48 << 10
+    opts = s2.make_opts(BF, grad_dtype=torch.float32, ds_max_mib=ds_mib)
+    assert s2.s2attn_workspace_size(1, B, L, Hq, Hkv, d, G, opts) > 2**32   # dS tiles kept
+    o, lse = s2.forward(tq, tk, tv, G, sh)
+    dq, dk, dv = s2.backward(tq, tk, tv, o, lse, tdo, G, sh, grad_dtype=torch.float32,
+                             ds_max_mib=ds_mib)
+    torch.cuda.synchronize()
+    n_g = L // G
+    units = [(0, 7, n_g - 1), (0, 15, n_g - 1), (0, 15, 0), (0, 0, n_g // 2)]
+    scale = 1.0 / math.sqrt(d)
+    f64 = lambda t: t.double().cpu().numpy()
+    tasks, rows_of = [], {}
+    for b, h, g in units:
+        rows = O.unit_rows(L, G, Hq, sh, h, g)
+        idx = torch.as_tensor(rows, device="cuda")
+        rows_of[(b, h, g)] = idx
+        tasks.append(((b, h, g), f64(tq[b, idx, h])[None], f64(tk[b, idx, h]), f64(tv[b, idx, h]),
+                      f64(tdo[b, idx, h])[None], scale, None))
+    ref = oracle_pool.kv_units_gathered(tasks)
+    for (b, h, g), idx in rows_of.items():
+        u = ref[(b, h, g)]
+        tag = f"unit ({b},{h},{g})"
+        check("o " + tag, f64(o[b, idx, h]), u["o"][0], BF16_REL_F, BF16_MAX_ABS)
+        check("lse " + tag, f64(lse[b, h, idx]), u["lse"][0], BF16_REL_F, BF16_MAX_ABS)
+        check("dq " + tag, f64(dq[b, idx, h]), u["dq"][0], BF16_REL_F, BF16_MAX_ABS)
+        check("dk " + tag, f64(dk[b, idx, h]), u["dk"], BF16_REL_F, BF16_MAX_ABS)
+        check("dv " + tag, f64(dv[b, idx, h]), u["dv"], BF16_REL_F, BF16_MAX_ABS)
+
+
 @pytest.mark.parametrize("name", ["fwd_bf16_causal_L32k", "fwd_bf16_causal_L100k"])
 def test_workload_dense_causal(name):
     """Dense causal attention (one group spanning the context, no shift), the
