@@ -484,6 +484,46 @@ def test_plane_at_the_32bit_offset_limit():
         check("dv " + tag, f64(dv[b, idx, h]), u["dv"], BF16_REL_F, BF16_MAX_ABS)
 
 
+def test_token_row_at_the_24bit_limit():
+    """Row offsets are formed as a 24-bit by 24-bit product of row index and
+    row bytes, so the host accepts token rows H d 2 below 2^24 bytes.  Here
+    65535 heads of d = 128 make a row of 2^24 - 256 bytes (one head more
+    reaches 2^24), with L = 64, G = 32 and half the heads shifted.  The
+    131070 units are not a multiple of the 8 XCDs, so the work decode takes
+    its unaligned form.  Units of the last heads (the largest offsets inside a
+    row), a shifted head's wrap group and the first unit match the oracle."""
+    import math
+    from tests import oracle_pool
+    B, L, Hq, Hkv, d, G, sh = 1, 64, 65535, 65535, 128, 32, 32768
+    assert Hq * d * 2 == 2**24 - 256 and (Hq + 1) * d * 2 == 2**24
+    say("[row limit] H=65535 d=128 L=64 G=32")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(53)
+    tq, tk, tv, tdo = (torch.randn((B, L, H, d), generator=gen, device="cuda").to(BF)
+                       for H in (Hq, Hkv, Hkv, Hq))
+    o, lse = s2.forward(tq, tk, tv, G, sh)
+    dq, dk, dv = s2.backward(tq, tk, tv, o, lse, tdo, G, sh, grad_dtype=torch.float32)
+    torch.cuda.synchronize()
+    units = [(0, Hq - 1, 1), (0, Hq - 1, 0), (0, Hq - sh - 1, 1), (0, 0, 0)]
+    scale = 1.0 / math.sqrt(d)
+    f64 = lambda t: t.double().cpu().numpy()
+    tasks, rows_of = [], {}
+    for b, h, g in units:
+        idx = torch.as_tensor(O.unit_rows(L, G, Hq, sh, h, g), device="cuda")
+        rows_of[(b, h, g)] = idx
+        tasks.append(((b, h, g), f64(tq[b, idx, h])[None], f64(tk[b, idx, h]), f64(tv[b, idx, h]),
+                      f64(tdo[b, idx, h])[None], scale, None))
+    ref = oracle_pool.kv_units_gathered(tasks)
+    for (b, h, g), idx in rows_of.items():
+        u = ref[(b, h, g)]
+        tag = f"unit ({b},{h},{g})"
+        check("o " + tag, f64(o[b, idx, h]), u["o"][0], BF16_REL_F, BF16_MAX_ABS)
+        check("lse " + tag, f64(lse[b, h, idx]), u["lse"][0], BF16_REL_F, BF16_MAX_ABS)
+        check("dq " + tag, f64(dq[b, idx, h]), u["dq"][0], BF16_REL_F, BF16_MAX_ABS)
+        check("dk " + tag, f64(dk[b, idx, h]), u["dk"], BF16_REL_F, BF16_MAX_ABS)
+        check("dv " + tag, f64(dv[b, idx, h]), u["dv"], BF16_REL_F, BF16_MAX_ABS)
+
+
 @pytest.mark.parametrize("name", ["fwd_bf16_causal_L32k", "fwd_bf16_causal_L100k"])
 def test_workload_dense_causal(name):
     """Dense causal attention (one group spanning the context, no shift), the
